@@ -1,0 +1,357 @@
+"""Pins for the fp64 oracle: checks against facts that do not come from the oracle itself.
+
+Each test names the fact it uses (a hand-written fixture, a closed form, brute
+force on a tiny input, an independent textbook routine, an invariant, or a
+finite-difference derivative).  No GPU needed.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_inputs import WORKLOADS, generate
+from dsa_inputs.configs import keep_to_k
+import oracle
+from oracle import Geometry
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def geom_of(wl):
+    return Geometry(*wl.latent, *wl.tile)
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = WORKLOADS["tiny_fp32"]
+    x = generate(wl)
+    return wl, {k: (f64(v) if v.is_floating_point() else v.numpy()) for k, v in x.items()}
+
+
+# ---------------------------------------------------------------- geometry
+def test_geometry_hand_fixture():
+    """Hand-written members (tests/golden/tiny_geometry.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "tiny_geometry.json")))
+    geom = Geometry(*g["latent"], *g["tile"])
+    assert geom.NB == g["NB"]
+    mem = geom.members()
+    for tau, toks in g["members"].items():
+        assert mem[int(tau)].tolist() == toks
+    dyn = g["dynamic_55k_tile0"]
+    geom2 = Geometry(*dyn["latent"], *dyn["tile"])
+    assert geom2.NB == dyn["NB"]
+    m0 = geom2.members()[0]
+    runs = [m0[i * dyn["run_length"]:(i + 1) * dyn["run_length"]] for i in range(len(m0) // dyn["run_length"])]
+    assert [int(r[0]) for r in runs] == [x[2] for x in dyn["first_run_per_frame_and_row"]]
+    assert all((np.diff(r) == 1).all() for r in runs)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "layer_32k", "dynamic_55k"])
+def test_geometry_partition(name):
+    """Every token lies in exactly one tile; each tile is a tt x th x tw box."""
+    wl = WORKLOADS[name]
+    geom = geom_of(wl)
+    mem = geom.members()
+    assert mem.shape == (wl.NB, wl.T)
+    flat = np.sort(mem.reshape(-1))
+    assert (flat == np.arange(wl.N)).all()
+    Lt, Lh, Lw = wl.latent
+    t, rem = np.divmod(mem, Lh * Lw)
+    y, x = np.divmod(rem, Lw)
+    for arr, ext in ((t, wl.tile[0]), (y, wl.tile[1]), (x, wl.tile[2])):
+        assert ((arr.max(1) - arr.min(1)) == ext - 1).all()
+        assert (arr.min(1) % ext == 0).all()
+    assert (np.diff(mem, axis=1) > 0).all()
+
+
+def test_block_counts():
+    assert [WORKLOADS[n].NB for n in ("tiny_fp32", "layer_32k", "long_524k", "train_32k", "dynamic_55k")] == \
+        [16, 512, 8192, 512, 864]
+    assert keep_to_k(10, 512) == 52 and keep_to_k(5, 8192) == 410
+    assert [keep_to_k(p, 864) for p in (2, 5, 10, 25)] == [18, 44, 87, 216]
+
+
+# ---------------------------------------------------------------- generator
+def test_splitmix64_known_answers():
+    from dsa_inputs.generator import mix64_int, GAMMA, raw_u64
+    g = json.load(open(os.path.join(GOLDEN, "splitmix64_seed0.json")))
+    want = [int(h, 16) for h in g["outputs_hex"]]
+    state, got = 0, []
+    for _ in range(3):
+        state = (state + GAMMA) & ((1 << 64) - 1)
+        got.append(mix64_int(state))
+    assert got == want
+    # the vectorised torch version gives the same bits (stream started at state 0 <=> s0 = 0)
+    from dsa_inputs import generator as G
+    s0_zero = G._s64(0)
+    i = torch.arange(1, 4, dtype=torch.int64)
+    vec = G.mix64_tensor(s0_zero + i * G._s64(GAMMA))
+    assert [int(v) & ((1 << 64) - 1) for v in vec] == want
+
+
+def test_generator_moments(tiny):
+    wl, x = tiny
+    assert abs(x["Wq"].std() * math.sqrt(wl.d) - 1) < 0.05
+    z = x["dO"].reshape(-1)
+    assert abs(z.mean()) < 0.02 and abs(z.std() - 1) < 0.02
+
+
+# ---------------------------------------------------------------- predictor
+def test_predictor_bruteforce_pairs(tiny):
+    """P-1: S[tau, j] is the mean over all (query-token, key-token) pairs of the
+    rank-r logits (q_i Wq) . (k_n Wk) -- computed pair by pair."""
+    wl, x = tiny
+    geom = geom_of(wl)
+    mem = geom.members()
+    for h in range(wl.H):
+        Q, K, Wq, Wk = x["Q"][0, h], x["K"][0, h], x["Wq"][h], x["Wk"][h]
+        _, _, S = oracle.predict_head(Q, K, Wq, Wk, mem)
+        for tau in (0, 3, 7, 15):
+            for j in (0, 5, 15):
+                acc = 0.0
+                for i in mem[tau]:
+                    qi = Q[i] @ Wq
+                    for n in mem[j]:
+                        acc += float(qi @ (K[n] @ Wk))
+                assert abs(S[tau, j] - acc / (len(mem[tau]) * len(mem[j]))) < 1e-12 * max(1.0, abs(acc))
+
+
+def test_predictor_pool_then_project(tiny):
+    """P-2: by linearity, pooling before projecting gives the same Qbar."""
+    wl, x = tiny
+    mem = geom_of(wl).members()
+    Q, Wq = x["Q"][0, 1], x["Wq"][1]
+    a = oracle.pooled_features(Q, Wq, mem)
+    b = Q[mem].mean(axis=1) @ Wq
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_predictor_homogeneity(tiny):
+    """P-3: scaling Wq by c scales S by c; swapping Q/K roles transposes S."""
+    wl, x = tiny
+    mem = geom_of(wl).members()
+    Q, K, Wq, Wk = x["Q"][0, 0], x["K"][0, 0], x["Wq"][0], x["Wk"][0]
+    _, _, S = oracle.predict_head(Q, K, Wq, Wk, mem)
+    _, _, S3 = oracle.predict_head(Q, K, 3.0 * Wq, Wk, mem)
+    assert np.abs(S3 - 3.0 * S).max() <= 1e-12 * np.abs(S).max()
+    _, _, St = oracle.predict_head(K, Q, Wk, Wq, mem)
+    assert np.abs(St - S.T).max() <= 1e-12 * np.abs(S).max()
+
+
+# ---------------------------------------------------------------- selection
+def brute_force_select(scores, tau, k):
+    """Max-sum subset of k-1 other blocks; equal sums -> lexicographically smallest."""
+    NB = len(scores)
+    others = [j for j in range(NB) if j != tau]
+    best, best_key = None, None
+    for sub in itertools.combinations(others, k - 1):       # ascending tuples
+        s = sum(scores[j] for j in sub)
+        key = (-s, sub)
+        if best_key is None or key < best_key:
+            best, best_key = sub, key
+    return sorted((tau,) + tuple(best))
+
+
+@pytest.mark.parametrize("kind", ["gaussian", "integer_ties"])
+def test_selection_bruteforce(kind):
+    """Brute force over all C(15, 3) = 455 candidate subsets (NB = 16, k = 4)."""
+    rng = np.random.default_rng(7)
+    for trial in range(12):
+        if kind == "gaussian":
+            row = rng.standard_normal(16)
+        else:
+            row = rng.integers(-2, 3, size=16).astype(np.float64)   # many exact ties
+        tau = int(rng.integers(0, 16))
+        assert oracle.select_row(row, tau, 4).tolist() == brute_force_select(row, tau, 4)
+
+
+def test_selection_invariants():
+    """I-1 size k, I-2 ascending distinct, I-3 own block, I-4 threshold property."""
+    rng = np.random.default_rng(3)
+    NB = 40
+    S = np.round(rng.standard_normal((NB, NB)), 1)    # rounding creates ties
+    for k in (1, 2, 7, 39, 40):
+        idx = oracle.select_head(S, k, kmax=k + 3)
+        for tau in range(NB):
+            row = idx[tau]
+            sel = row[:k]
+            assert (row[k:] == -1).all()
+            assert len(sel) == k and (np.diff(sel) > 0).all()
+            assert tau in sel and sel.min() >= 0 and sel.max() < NB
+            chosen = [j for j in sel if j != tau]
+            rest = [j for j in range(NB) if j != tau and j not in sel]
+            if chosen and rest:
+                worst_in = min(chosen, key=lambda j: (S[tau, j], -j))
+                for j in rest:
+                    assert S[tau, worst_in] > S[tau, j] or (S[tau, worst_in] == S[tau, j] and worst_in < j)
+
+
+def test_selection_zero_scores_fixture():
+    """Q = 0 gives S = 0; the hand-written fixture lists the lowest-index picks."""
+    g = json.load(open(os.path.join(GOLDEN, "tiny_zero_q_selection.json")))
+    S = np.zeros((g["NB"], g["NB"]))
+    for tau, want in g["rows"].items():
+        assert oracle.select_row(S[int(tau)], int(tau), g["k"]).tolist() == want
+
+
+def test_selection_extremes():
+    rng = np.random.default_rng(11)
+    S = rng.standard_normal((16, 16))
+    for tau in range(16):
+        assert oracle.select_row(S[tau], tau, 16).tolist() == list(range(16))
+        assert oracle.select_row(S[tau], tau, 1).tolist() == [tau]
+
+
+# ---------------------------------------------------------------- forward
+def dense_attention_torch(Q, K, V, scale):
+    """Textbook dense softmax attention, written independently (torch fp64, CPU)."""
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a)) for a in (Q, K, V))
+    logits = (q @ k.transpose(0, 1)) * scale
+    return (torch.softmax(logits, dim=-1) @ v).numpy(), torch.logsumexp(logits, dim=-1).numpy()
+
+
+def test_keep_all_equals_dense(tiny):
+    """k = NB (keep fraction 1.0) must equal dense attention (tiny workload)."""
+    wl, x = tiny
+    geom = geom_of(wl)
+    mem = geom.members()
+    scale = 1 / math.sqrt(wl.d)
+    NB = geom.NB
+    for h in range(wl.H):
+        Q, K, V = x["Q"][0, h], x["K"][0, h], x["V"][0, h]
+        idx = np.tile(np.arange(NB, dtype=np.int32), (NB, 1))
+        O, LSE = oracle.attn_fwd_head(Q, K, V, mem, idx, NB, scale)
+        Od, Ld = dense_attention_torch(Q, K, V, scale)
+        assert np.abs(O - Od).max() < 1e-12
+        assert np.abs(LSE - Ld).max() < 1e-12
+
+
+def test_zero_query_closed_form(tiny):
+    """Q = 0: uniform weights, so O is the mean of the kept V rows and LSE = ln(k T)."""
+    wl, x = tiny
+    geom = geom_of(wl)
+    mem = geom.members()
+    rng = np.random.default_rng(5)
+    k = 4
+    idx = np.full((geom.NB, k), -1, np.int32)
+    for tau in range(geom.NB):
+        others = rng.choice([j for j in range(geom.NB) if j != tau], k - 1, replace=False)
+        idx[tau] = np.sort(np.concatenate(([tau], others)))
+    Q = np.zeros_like(x["Q"][0, 0])
+    O, LSE = oracle.attn_fwd_head(Q, x["K"][0, 0], x["V"][0, 0], mem, idx, k, 0.125)
+    assert np.abs(LSE - 4.158883083359672).max() < 1e-12     # ln 64, 64 = 4 blocks x 16 tokens
+    for tau in range(geom.NB):
+        keys = np.concatenate([mem[j] for j in idx[tau]])
+        want = x["V"][0, 0][keys].mean(axis=0)
+        assert np.abs(O[mem[tau]] - want).max() < 1e-12
+
+
+def test_constant_values_and_shift_invariance(tiny):
+    """V = c gives O = c; adding one vector u to every key shifts each row's
+    logits by a constant, leaving O unchanged and shifting LSE by scale q.u."""
+    wl, x = tiny
+    mem = geom_of(wl).members()
+    Q, K, V = x["Q"][0, 1], x["K"][0, 1], x["V"][0, 1]
+    S = oracle.predict_head(Q, K, x["Wq"][1], x["Wk"][1], mem)[2]
+    idx = oracle.select_head(S, 5, 5)
+    scale = 1 / math.sqrt(wl.d)
+    O, LSE = oracle.attn_fwd_head(Q, K, np.full_like(V, 2.5), mem, idx, 5, scale)
+    assert np.abs(O - 2.5).max() < 1e-12
+    O1, L1 = oracle.attn_fwd_head(Q, K, V, mem, idx, 5, scale)
+    u = np.random.default_rng(1).standard_normal(wl.d)
+    O2, L2 = oracle.attn_fwd_head(Q, K + u, V, mem, idx, 5, scale)
+    assert np.abs(O1 - O2).max() < 1e-11
+    assert np.abs((L2 - L1) - scale * (Q @ u)).max() < 1e-11
+
+
+def test_softmax_rows_sum_to_one(tiny):
+    """I-5 rows of P sum to 1; I-6 the unnormalised sum is at least 1."""
+    wl, x = tiny
+    mem = geom_of(wl).members()
+    scale = 1 / math.sqrt(wl.d)
+    for tau in range(16):
+        blocks = sorted({tau, (tau + 3) % 16, (tau + 7) % 16})
+        _, LSE, P, keys = oracle.attn_tile(x["Q"][0, 0], x["K"][0, 0], x["V"][0, 0], mem, tau, blocks, scale)
+        assert np.abs(P.sum(1) - 1).max() < 1e-12
+        s = x["Q"][0, 0][mem[tau]] @ x["K"][0, 0][keys].T * scale
+        ell = np.exp(s - s.max(1, keepdims=True)).sum(1)
+        assert (ell >= 1).all()
+
+
+# ---------------------------------------------------------------- backward
+def test_backward_finite_differences(tiny):
+    """Central differences of L = sum(O * dO) in fp64 (step 1e-5)."""
+    wl, x = tiny
+    geom = geom_of(wl)
+    mem = geom.members()
+    h = 0
+    Q, K, V, dO = (x[n][0, h].copy() for n in ("Q", "K", "V", "dO"))
+    S = oracle.predict_head(Q, K, x["Wq"][h], x["Wk"][h], mem)[2]
+    k = 4
+    idx = oracle.select_head(S, k, k)
+    scale = 1 / math.sqrt(wl.d)
+    dQ, dK, dV = oracle.attn_bwd_head(Q, K, V, dO, mem, idx, k, scale)
+
+    def loss(Qx, Kx, Vx):
+        O, _ = oracle.attn_fwd_head(Qx, Kx, Vx, mem, idx, k, scale)
+        return float((O * dO).sum())
+
+    rng = np.random.default_rng(2)
+    eps = 1e-5
+    for name, grad in (("Q", dQ), ("K", dK), ("V", dV)):
+        for _ in range(6):
+            n, e = int(rng.integers(0, wl.N)), int(rng.integers(0, wl.d))
+            args = {"Q": Q, "K": K, "V": V}
+            plus = {kk: vv.copy() for kk, vv in args.items()}
+            minus = {kk: vv.copy() for kk, vv in args.items()}
+            plus[name][n, e] += eps
+            minus[name][n, e] -= eps
+            fd = (loss(plus["Q"], plus["K"], plus["V"]) - loss(minus["Q"], minus["K"], minus["V"])) / (2 * eps)
+            assert abs(fd - grad[n, e]) < 1e-7 * max(1.0, abs(fd)), (name, n, e, fd, grad[n, e])
+
+
+def test_backward_invariants(tiny):
+    """I-7 sum_n dS_in = 0; I-8 sum dV = sum dO; I-9 sum dK = 0; I-10 in-degree >= 1."""
+    wl, x = tiny
+    mem = geom_of(wl).members()
+    scale = 1 / math.sqrt(wl.d)
+    for h in range(wl.H):
+        Q, K, V, dO = (x[n][0, h] for n in ("Q", "K", "V", "dO"))
+        S = oracle.predict_head(Q, K, x["Wq"][h], x["Wk"][h], mem)[2]
+        idx = oracle.select_head(S, 4, 4)
+        indeg = np.bincount(idx.reshape(-1), minlength=16)
+        assert (indeg >= 1).all()
+        for tau in range(16):
+            *_, dS = oracle.attn_bwd_tile(Q, K, V, dO, mem, tau, list(idx[tau]), scale)
+            assert np.abs(dS.sum(1)).max() < 1e-12
+        dQ, dK, dV = oracle.attn_bwd_head(Q, K, V, dO, mem, idx, 4, scale)
+        assert np.abs(dV.sum(0) - dO.sum(0)).max() < 1e-10
+        assert np.abs(dK.sum(0)).max() < 1e-10
+        # the per-key-block helper agrees with the full backward
+        for j in (0, 9):
+            dKj, dVj = oracle.attn_bwd_key_block(Q, K, V, dO, mem, idx, 4, scale, j)
+            assert np.abs(dKj - dK[mem[j]]).max() < 1e-12 and np.abs(dVj - dV[mem[j]]).max() < 1e-12
+
+
+def test_keep_all_gradients_equal_dense_autograd(tiny):
+    """k = NB: gradients equal torch autograd of dense attention (fp64, CPU)."""
+    wl, x = tiny
+    mem = geom_of(wl).members()
+    scale = 1 / math.sqrt(wl.d)
+    h = 1
+    Q, K, V, dO = (x[n][0, h] for n in ("Q", "K", "V", "dO"))
+    idx = np.tile(np.arange(16, dtype=np.int32), (16, 1))
+    dQ, dK, dV = oracle.attn_bwd_head(Q, K, V, dO, mem, idx, 16, scale)
+    q, k, v = (torch.tensor(a, requires_grad=True) for a in (Q, K, V))
+    out = torch.softmax((q @ k.T) * scale, dim=-1) @ v
+    (out * torch.from_numpy(dO)).sum().backward()
+    for mine, ref in ((dQ, q.grad), (dK, k.grad), (dV, v.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-11
