@@ -1,0 +1,212 @@
+"""DSV-style dynamic block-sparse attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libdsa.so`` (declared in
+``include/dsa.h``).  It only marshals arguments: PyTorch supplies device
+memory and the current HIP stream; every step of the path (predictor scores,
+top-k selection, block-sparse attention forward and backward) runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+
+Method: DSV: Exploiting Dynamic Sparsity to Accelerate Large-Scale Video DiT
+Training (gist.science/ar/paper/2502.07590) -- a low-rank predictor (section 3a)
+scores query-tile x key-block pairs, each tile of neighbouring queries keeps
+its top-k key blocks (section 3b), and exact attention runs only over those
+(section 4).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
+    "bwd_workspace_bytes", "DsaError", "F32", "BF16",
+]
+
+F32 = 0
+BF16 = 1
+_LIB_NAME = "libdsa.so"
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "d", "Lt", "Lh", "Lw", "tt", "th", "tw", "io")]
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m dynamic_sparse_attention_lowrank_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(library_path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    sp = ctypes.POINTER(Shape)
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_status_string.argtypes = [ctypes.c_int]
+    L.dsa_version.restype = i32
+    L.dsa_version.argtypes = []
+    L.dsa_predict.restype = ctypes.c_int
+    L.dsa_predict.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dsa_select.restype = ctypes.c_int
+    L.dsa_select.argtypes = [sp, vp, vp, i32, vp, vp]
+    L.dsa_attn_fwd.restype = ctypes.c_int
+    L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp]
+    L.dsa_attn_bwd_workspace_bytes.restype = sz
+    L.dsa_attn_bwd_workspace_bytes.argtypes = [sp, i32]
+    L.dsa_attn_bwd.restype = ctypes.c_int
+    L.dsa_attn_bwd.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+    return L
+
+
+lib = _load()
+
+
+@dataclass(frozen=True)
+class Layout:
+    """Latent grid and tile of a video-token sequence (tokens row-major over (t, y, x))."""
+    latent: Tuple[int, int, int]
+    tile: Tuple[int, int, int]
+
+    @property
+    def N(self) -> int:
+        return self.latent[0] * self.latent[1] * self.latent[2]
+
+    @property
+    def T(self) -> int:
+        return self.tile[0] * self.tile[1] * self.tile[2]
+
+    @property
+    def NB(self) -> int:
+        return self.N // self.T
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _shape(X: torch.Tensor, layout: Layout) -> Shape:
+    if X.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    B, H, N, d = X.shape
+    if N != layout.N:
+        raise ValueError(f"tensor has N={N} tokens but the latent {layout.latent} holds {layout.N}")
+    return Shape(B, H, d, *layout.latent, *layout.tile, _io_code(X))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsaError(status, lib.dsa_status_string(status).decode())
+
+
+def predict(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, layout: Layout,
+            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Low-rank predictor: returns (Qbar, Kbar, S) as float32 [B,H,NB,r], [B,H,NB,r], [B,H,NB,NB]."""
+    _dev(Q, K, Wq, Wk)
+    sh = _shape(Q, layout)
+    B, H = Q.shape[:2]
+    r = Wq.shape[-1]
+    if out is None:
+        Qbar = torch.empty(B, H, layout.NB, r, device=Q.device, dtype=torch.float32)
+        Kbar = torch.empty_like(Qbar)
+        S = torch.empty(B, H, layout.NB, layout.NB, device=Q.device, dtype=torch.float32)
+    else:
+        Qbar, Kbar, S = out
+    _check(lib.dsa_predict(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(Qbar), _ptr(Kbar),
+                           _ptr(S), _stream()))
+    return Qbar, Kbar, S
+
+
+def select(S: torch.Tensor, k: torch.Tensor, kmax: int, layout: Layout, d: int = 128,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k key blocks per query tile: idx int32 [B,H,NB,kmax], ascending, -1 padded."""
+    _dev(S, k)
+    B, H = S.shape[:2]
+    sh = Shape(B, H, d, *layout.latent, *layout.tile, F32)
+    idx = out if out is not None else torch.empty(B, H, layout.NB, kmax, device=S.device, dtype=torch.int32)
+    _check(lib.dsa_select(ctypes.byref(sh), _ptr(S), _ptr(k), kmax, _ptr(idx), _stream()))
+    return idx
+
+
+def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, k: torch.Tensor, layout: Layout,
+             scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+             out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Block-sparse attention forward: returns (O [B,H,N,d] out_dtype, LSE [B,H,N] float32)."""
+    _dev(Q, K, V, idx, k)
+    sh = _shape(Q, layout)
+    kmax = idx.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Q.shape[-1])
+    odt = out_dtype or Q.dtype
+    if out is None:
+        O = torch.empty(Q.shape, device=Q.device, dtype=odt)
+        LSE = torch.empty(Q.shape[:3], device=Q.device, dtype=torch.float32)
+    else:
+        O, LSE = out
+    _check(lib.dsa_attn_fwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
+                            _io_code(O), _ptr(O), _ptr(LSE), _stream()))
+    return O, LSE
+
+
+def bwd_workspace_bytes(Q: torch.Tensor, layout: Layout, kmax: int) -> int:
+    sh = _shape(Q, layout)
+    return int(lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
+
+
+def attn_bwd(Q, K, V, O, dO, LSE, idx, k, layout: Layout, scale: Optional[float] = None,
+             out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+             out: Optional[Sequence[torch.Tensor]] = None):
+    """Block-sparse attention backward (mask fixed): returns (dQ, dK, dV).
+
+    O may be float32 or bfloat16 (the forward output); float32 keeps D = dO . O
+    accurate."""
+    _dev(Q, K, V, O, dO, LSE, idx, k)
+    sh = _shape(Q, layout)
+    kmax = idx.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Q.shape[-1])
+    odt = out_dtype or Q.dtype
+    if out is None:
+        dQ = torch.empty(Q.shape, device=Q.device, dtype=odt)
+        dK = torch.empty_like(dQ)
+        dV = torch.empty_like(dQ)
+    else:
+        dQ, dK, dV = out
+    need = int(lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
+    _check(lib.dsa_attn_bwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _io_code(O), _ptr(dO), _ptr(LSE),
+                            _ptr(idx),
+                            _ptr(k), kmax, scale, _io_code(dQ), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream()))
+    return dQ, dK, dV

@@ -1,0 +1,178 @@
+// C ABI of libdsa (declared in include/dsa.h): argument checks on the host,
+// shape derivation, workspace carving and kernel launches.  No entry point
+// allocates memory, synchronises the device or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include "dsa.h"
+#include "kernels.hpp"
+
+using namespace dsa;
+
+namespace {
+
+struct Derived {
+  Geo g;
+  int BH;
+  int d;
+  int io_f32;
+};
+
+dsa_status derive(const dsa_shape* s, Derived* out) {
+  if (s == nullptr) return DSA_ERR_NULL;
+  if (s->io != DSA_F32 && s->io != DSA_BF16) return DSA_ERR_DTYPE;
+  if (s->B < 0 || s->H < 0) return DSA_ERR_SHAPE;
+  if (s->d != 64 && s->d != 128) return DSA_ERR_SHAPE;
+  if (s->Lt < 1 || s->Lh < 1 || s->Lw < 1) return DSA_ERR_SHAPE;
+  if (s->tt < 1 || s->th < 1 || s->tw < 1) return DSA_ERR_TILE;
+  if (s->Lt % s->tt || s->Lh % s->th || s->Lw % s->tw) return DSA_ERR_TILE;
+  const int64_t T = (int64_t)s->tt * s->th * s->tw;
+  if (T > 64) return DSA_ERR_TILE;
+  const int64_t N = (int64_t)s->Lt * s->Lh * s->Lw;
+  if (N * s->d > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  const int64_t NB = N / T;
+  const int64_t BH = (int64_t)s->B * s->H;
+  if (BH > 65535 || BH * NB > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  Geo g;
+  g.Lt = s->Lt; g.Lh = s->Lh; g.Lw = s->Lw;
+  g.tt = s->tt; g.th = s->th; g.tw = s->tw;
+  g.gt = s->Lt / s->tt; g.gh = s->Lh / s->th; g.gw = s->Lw / s->tw;
+  g.N = (int)N; g.T = (int)T; g.NB = (int)NB;
+  out->g = g;
+  out->BH = (int)BH;
+  out->d = s->d;
+  out->io_f32 = s->io == DSA_F32;
+  return DSA_OK;
+}
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t dvec, bitmap, counts, offsets, entries, total;
+  int words;
+};
+
+BwdLayout bwd_layout(const Derived& dv, int kmax) {
+  BwdLayout l;
+  const size_t BH = (size_t)dv.BH, N = (size_t)dv.g.N, NB = (size_t)dv.g.NB;
+  l.words = (int)((NB + 31) / 32);
+  size_t off = 0;
+  l.dvec = off;    off += align256(BH * N * sizeof(float));
+  l.bitmap = off;  off += align256(BH * NB * (size_t)l.words * sizeof(uint32_t));
+  l.counts = off;  off += align256(BH * NB * sizeof(int32_t));
+  l.offsets = off; off += align256(BH * (NB + 1) * sizeof(int32_t));
+  l.entries = off; off += align256(BH * NB * (size_t)kmax * sizeof(int32_t));
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: unsupported B, H, N or d";
+    case DSA_ERR_TILE: return "DSA_ERR_TILE: tile does not divide the latent or holds more than 64 tokens";
+    case DSA_ERR_K: return "DSA_ERR_K: kmax out of range";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: unknown element type";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace too small, NULL or not 256-byte aligned";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP launch failed";
+    case DSA_ERR_NOT_IMPLEMENTED: return "DSA_ERR_NOT_IMPLEMENTED";
+    case DSA_ERR_RANK: return "DSA_ERR_RANK: predictor rank must be in [1, 64]";
+  }
+  return "unknown dsa_status";
+}
+
+int32_t dsa_version(void) { return 100; }
+
+dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q, const void* K, const void* Wq,
+                       const void* Wk, float* Qbar, float* Kbar, float* S, hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (r < 1 || r > 64) return DSA_ERR_RANK;
+  if (dv.BH == 0) return DSA_OK;
+  if (!Q || !K || !Wq || !Wk || !Qbar || !Kbar || !S) return DSA_ERR_NULL;
+  PredictArgs a;
+  a.Q = Q; a.K = K; a.Wq = Wq; a.Wk = Wk;
+  a.Qbar = Qbar; a.Kbar = Kbar; a.S = S;
+  a.g = dv.g; a.B = shape->B; a.H = shape->H; a.r = r;
+  return hip_status(launch_predict(a, dv.io_f32, dv.d, stream));
+}
+
+dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, int32_t kmax, int32_t* idx,
+                      hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
+  if (dv.BH == 0) return DSA_OK;
+  if (!S || !k || !idx) return DSA_ERR_NULL;
+  SelectArgs a;
+  a.S = S; a.kvec = k; a.kmax = kmax; a.idx = idx; a.NB = dv.g.NB; a.BH = dv.BH;
+  return hip_status(launch_select(a, stream));
+}
+
+dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, const void* V, const int32_t* idx,
+                        const int32_t* k, int32_t kmax, float scale, int32_t out_dtype, void* O, float* LSE,
+                        hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
+  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  if (dv.BH == 0) return DSA_OK;
+  if (!Q || !K || !V || !idx || !k || !O || !LSE) return DSA_ERR_NULL;
+  FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.idx = idx; a.kvec = k; a.kmax = kmax;
+  a.O = O; a.LSE = LSE; a.out_f32 = out_dtype == DSA_F32;
+  a.c = scale * kLog2e;
+  a.g = dv.g; a.BH = dv.BH;
+  return hip_status(launch_attn_fwd(a, dv.io_f32, dv.d, stream));
+}
+
+size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax) {
+  Derived dv;
+  if (derive(shape, &dv) != DSA_OK) return 0;
+  if (kmax < 1 || kmax > dv.g.NB) return 0;
+  return bwd_layout(dv, kmax).total;
+}
+
+dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V, const void* O,
+                        int32_t o_dtype, const void* dO, const float* LSE, const int32_t* idx, const int32_t* k, int32_t kmax,
+                        float scale, int32_t out_dtype, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (o_dtype != DSA_F32 && o_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
+  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  if (dv.BH == 0) return DSA_OK;
+  if (!Q || !K || !V || !O || !dO || !LSE || !idx || !k || !dQ || !dK || !dV) return DSA_ERR_NULL;
+  const BwdLayout l = bwd_layout(dv, kmax);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255u)) return DSA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.o_f32 = o_dtype == DSA_F32; a.dO = dO; a.LSE = LSE;
+  a.idx = idx; a.kvec = k; a.kmax = kmax;
+  a.scale = scale; a.c = scale * kLog2e; a.out_f32 = out_dtype == DSA_F32;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.Dvec = reinterpret_cast<float*>(ws + l.dvec);
+  a.bitmap = reinterpret_cast<uint32_t*>(ws + l.bitmap);
+  a.counts = reinterpret_cast<int32_t*>(ws + l.counts);
+  a.offsets = reinterpret_cast<int32_t*>(ws + l.offsets);
+  a.entries = reinterpret_cast<int32_t*>(ws + l.entries);
+  a.words = l.words;
+  a.g = dv.g; a.BH = dv.BH;
+  return hip_status(launch_attn_bwd(a, dv.io_f32, dv.d, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,424 @@
+// Block-sparse attention backward for gfx950, block mask held fixed.
+//
+// The DSV page (gist.science/ar/paper/2502.07590) trains the video DiT with the
+// sparse attention in its second stage (section 4), so the kept blocks need
+// exact gradients: with P recomputed from the forward's log-sum-exp,
+//   D_i = dO_i . O_i,  dS_in = P_in (dO_i . v_n - D_i),
+//   dQ_i = scale sum_n dS_in k_n,  dK_n = scale sum_i dS_in q_i,  dV_n = sum_i P_in dO_i.
+//
+// Precision: the probabilities P and dS are computed in fp32 inside the
+// kernels; where they feed a matrix-core product with bf16 inputs they are
+// carried as a bf16 pair (hi + lo, see common.hpp) and the product is issued
+// twice, so the gradients keep fp32-level accuracy whatever the scale of dO.
+// D is taken from O as passed in (fp32 O keeps D accurate; with bf16 O its
+// rounding enters D coherently across a whole row).
+//
+// No floating-point atomics, so results are bit-reproducible:
+//   1. prep:     D (fp32) for every token;
+//   2. reverse index of the block mask: a bitmap row per key block (bit tau set
+//      if tile tau kept it; integer OR is order-free), popcounts, a per-head
+//      exclusive scan, and an ascending compaction into CSC lists;
+//   3. dK/dV:    one work-group per key block walks the query tiles that kept it
+//                (S = Q K^T and dP = dO V^T with K, V in registers; then
+//                dV += P^T dO and dK += dS^T Q from transposed Q/dO tiles in LDS);
+//   4. dQ:       one work-group per query tile walks its kept blocks like the
+//                forward (S^T = K Q^T, dP^T = V dO^T; dQ^T += K^T dS^T).
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace dsa {
+
+namespace {
+
+// ---------------------------------------------------------------- 1. D = rowsum(dO * O)
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int CE = Elem<T>::kChunkElems;
+  constexpr int CPR = D / CE;                 // lanes per token
+  constexpr int TPB = 256 / CPR;              // tokens per work-group
+  const size_t total = (size_t)a.BH * a.g.N;
+  const size_t tok = (size_t)blockIdx.x * TPB + threadIdx.x / CPR;
+  const int c = threadIdx.x % CPR;
+  float s = 0.f;
+  if (tok < total) {
+    const u32x4 g = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.dO) + tok * D + c * CE);
+    const T* gv = reinterpret_cast<const T*>(&g);
+    float ov[CE];
+    if (a.o_f32) {
+      const float* O = reinterpret_cast<const float*>(a.O) + tok * D + c * CE;
+#pragma unroll
+      for (int q = 0; q < CE / 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(O + 4 * q);
+        ov[4 * q] = v[0]; ov[4 * q + 1] = v[1]; ov[4 * q + 2] = v[2]; ov[4 * q + 3] = v[3];
+      }
+    } else {
+      const bf16* O = reinterpret_cast<const bf16*>(a.O) + tok * D + c * CE;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) ov[e] = (float)O[e];
+    }
+#pragma unroll
+    for (int e = 0; e < CE; ++e) s = fmaf(ov[e], to_f32(gv[e]), s);
+  }
+#pragma unroll
+  for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (tok < total && c == 0) a.Dvec[tok] = s;
+}
+
+// ---------------------------------------------------------------- 2. reverse index
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void rev_setbits_kernel(BwdArgs a) {
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int NB = a.g.NB;
+  if (id >= (size_t)a.BH * NB * a.kmax) return;
+  const int slot = (int)(id % a.kmax);
+  const size_t row = id / a.kmax;             // bh * NB + tau
+  const int bh = (int)(row / NB);
+  const int tau = (int)(row % NB);
+  int kk = a.kvec[bh];
+  kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
+  if (slot >= kk) return;
+  const int j = a.idx[id];
+  if ((unsigned)j >= (unsigned)NB) return;
+  atomicOr(&a.bitmap[((size_t)bh * NB + j) * a.words + (tau >> 5)], 1u << (tau & 31));
+}
+
+// one wave per (head, key block)
+__global__ __launch_bounds__(256) void rev_count_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)a.BH * a.g.NB) return;
+  const uint32_t* w = a.bitmap + row * a.words;
+  int cnt = 0;
+  for (int i = lane; i < a.words; i += 64) cnt += __popc(w[i]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
+  if (lane == 0) a.counts[row] = cnt;
+}
+
+// one work-group per head: offsets[bh][j] = sum of counts before j; offsets[bh][NB] = total
+__global__ __launch_bounds__(1024) void rev_scan_kernel(BwdArgs a) {
+  __shared__ int part[1024];
+  const int NB = a.g.NB;
+  const int bh = blockIdx.x;
+  const int* cnt = a.counts + (size_t)bh * NB;
+  int* off = a.offsets + (size_t)bh * (NB + 1);
+  const int per = (NB + 1023) / 1024;
+  const int lo = threadIdx.x * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i) s += (lo + i < NB) ? cnt[lo + i] : 0;
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {        // Hillis-Steele inclusive scan
+    const int v = threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;            // exclusive prefix of this thread's range
+  for (int i = 0; i < per; ++i) {
+    if (lo + i < NB) {
+      off[lo + i] = run;
+      run += cnt[lo + i];
+    }
+  }
+  if (threadIdx.x == 1023) off[NB] = part[1023];
+}
+
+// one wave per (head, key block): set bits in ascending order -> entries
+__global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int NB = a.g.NB;
+  if (row >= (size_t)a.BH * NB) return;
+  const int bh = (int)(row / NB);
+  const int j = (int)(row % NB);
+  const uint32_t* w = a.bitmap + row * a.words;
+  int32_t* out = a.entries + (size_t)bh * NB * a.kmax + a.offsets[(size_t)bh * (NB + 1) + j];
+  int done = 0;
+  for (int base = 0; base < a.words; base += 64) {
+    const int i = base + lane;
+    uint32_t word = i < a.words ? w[i] : 0u;
+    const int pc = __popc(word);
+    int incl = pc;                              // inclusive prefix over lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    int pos = done + incl - pc;
+    while (word) {
+      const int b = __ffs(word) - 1;
+      out[pos++] = 32 * i + b;
+      word &= word - 1u;
+    }
+    done += __shfl(incl, 63, 64);
+  }
+}
+
+// ---------------------------------------------------------------- 3. dK, dV
+template <typename T, int D>
+__global__ __launch_bounds__(kTileThreads) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = TileCfg<T, D>;
+  typedef typename Elem<T>::frag Frag;
+  __shared__ u32x4 lds_q[C::kRowChunks];
+  __shared__ u32x4 lds_qt[C::kTrChunks];
+  __shared__ u32x4 lds_g[C::kRowChunks];
+  __shared__ u32x4 lds_gt[C::kTrChunks];
+  __shared__ float lds_lse[64];
+  __shared__ float lds_dv[64];
+
+  const Geo g = a.g;
+  const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
+  const int bh = L / g.NB;
+  const int j = L - bh * g.NB;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const size_t head_off = (size_t)bh * g.N * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(a.Q) + head_off;
+  const T* __restrict__ Gh = reinterpret_cast<const T*>(a.dO) + head_off;
+  const int jbase = tile_base(g, j);
+
+  // this lane's key row as B fragments (S = Q K^T, dP = dO V^T: N = keys)
+  const int kr = 32 * wave + l32;
+  const bool k_ok = kr < g.T;
+  const int k_tok = jbase + (k_ok ? member_offset(g, kr) : 0);
+  Frag kf[C::kSteps], vf[C::kSteps];
+  load_row_frags<T, D>(kf, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, h);
+  load_row_frags<T, D>(vf, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, h);
+
+  int goff[C::kGPer][8];
+  group_offsets<T, D>(goff, g, tid);
+  int qmo = -1;                                   // member offset of query row tid (tid < 64)
+  if (tid < 64 && tid < g.T) qmo = member_offset(g, tid);
+
+  f32x16 dkacc[C::kDTiles], dvacc[C::kDTiles];
+#pragma unroll
+  for (int t = 0; t < C::kDTiles; ++t) {
+    dkacc[t] = f32x16{};
+    dvacc[t] = f32x16{};
+  }
+  const float c2 = a.c;
+  const int* list = a.entries + (size_t)bh * g.NB * a.kmax;
+  const int* off = a.offsets + (size_t)bh * (g.NB + 1);
+  const int e0 = off[j], e1 = off[j + 1];
+
+  GroupStage<T, D> qst, gst;
+  for (int e = e0; e < e1; ++e) {
+    const int tau = list[e];
+    const int base = tile_base(g, tau);
+    group_load<T, D>(qst, Qh, base, goff, tid);
+    group_load<T, D>(gst, Gh, base, goff, tid);
+    group_store<T, D>(qst, lds_qt, lds_q, tid);     // the previous pass ended with a barrier
+    group_store<T, D>(gst, lds_gt, lds_g, tid);
+    if (tid < 64) {
+      const size_t t_idx = (size_t)bh * g.N + base + (qmo >= 0 ? qmo : 0);
+      lds_lse[tid] = qmo >= 0 ? a.LSE[t_idx] * kLog2e : INFINITY;
+      lds_dv[tid] = qmo >= 0 ? a.Dvec[t_idx] : 0.f;
+    }
+    __syncthreads();
+
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = f32x16{};
+      pacc[mt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        sacc[mt] = mma_step(frag_row<T, D>(lds_q, 32 * mt + l32, s, h), kf[s], sacc[mt]);
+        pacc[mt] = mma_step(frag_row<T, D>(lds_g, 32 * mt + l32, s, h), vf[s], pacc[mt]);
+      }
+    }
+    // P and dS; lane holds key column kr, query rows 32mt + 8g + 4h + i
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int q0 = 32 * mt + 8 * gq + 4 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(fmaf(sacc[mt][4 * gq + i], c2, -lds_lse[q0 + i]));
+          sacc[mt][4 * gq + i] = p;
+          pacc[mt][4 * gq + i] = p * (pacc[mt][4 * gq + i] - lds_dv[q0 + i]);
+        }
+      }
+    }
+    typename SplitOf<T>::type pf[4], sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float pv[8], sv[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        pv[e2] = sacc[s >> 1][8 * (s & 1) + e2];
+        sv[e2] = pacc[s >> 1][8 * (s & 1) + e2];
+      }
+      to_split(pv, pf[s]);
+      to_split(sv, sf[s]);
+    }
+#pragma unroll
+    for (int t = 0; t < C::kDTiles; ++t) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        dvacc[t] = mma_split_a(pf[s], frag_tr<T, D>(lds_gt, 32 * t + l32, s, h), dvacc[t]);
+        dkacc[t] = mma_split_a(sf[s], frag_tr<T, D>(lds_qt, 32 * t + l32, s, h), dkacc[t]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // store: lane holds d column 32t + l32, key rows 32*wave + 8g + 4h + i
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * wave + 8 * gq + 4 * h + i;
+      if (r < g.T) {
+        const size_t orow = head_off + (size_t)(jbase + member_offset(g, r)) * D;
+#pragma unroll
+        for (int t = 0; t < C::kDTiles; ++t) {
+          store1(a.dK, orow + 32 * t + l32, a.out_f32, a.scale * dkacc[t][4 * gq + i]);
+          store1(a.dV, orow + 32 * t + l32, a.out_f32, dvacc[t][4 * gq + i]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 4. dQ
+template <typename T, int D>
+__global__ __launch_bounds__(kTileThreads) void bwd_dq_kernel(BwdArgs a) {
+  using C = TileCfg<T, D>;
+  typedef typename Elem<T>::frag Frag;
+  __shared__ u32x4 lds_k[C::kRowChunks];
+  __shared__ u32x4 lds_kt[C::kTrChunks];
+  __shared__ u32x4 lds_v[C::kRowChunks];
+
+  const Geo g = a.g;
+  const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
+  const int bh = L / g.NB;
+  const int tau = L - bh * g.NB;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const size_t head_off = (size_t)bh * g.N * D;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(a.K) + head_off;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + head_off;
+  const int* __restrict__ irow = a.idx + ((size_t)bh * g.NB + tau) * a.kmax;
+  int kk = a.kvec[bh];
+  kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
+
+  const int q = 32 * wave + l32;
+  const bool q_ok = q < g.T;
+  const int q_tok = tile_base(g, tau) + (q_ok ? member_offset(g, q) : 0);
+  Frag qf[C::kSteps], gf[C::kSteps];
+  load_row_frags<T, D>(qf, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, h);
+  load_row_frags<T, D>(gf, reinterpret_cast<const T*>(a.dO) + head_off + (size_t)q_tok * D, q_ok, h);
+  const float lse2 = q_ok ? a.LSE[(size_t)bh * g.N + q_tok] * kLog2e : INFINITY;
+  const float dv = q_ok ? a.Dvec[(size_t)bh * g.N + q_tok] : 0.f;
+
+  int koff[C::kGPer][8];
+  group_offsets<T, D>(koff, g, tid);
+  int voff[C::kRowPer];
+  row_offsets<T, D>(voff, g, tid);
+
+  f32x16 dqacc[C::kDTiles];
+#pragma unroll
+  for (int t = 0; t < C::kDTiles; ++t) dqacc[t] = f32x16{};
+  const float c2 = a.c;
+
+  int slot = 0;
+  while (slot < kk && (unsigned)irow[slot] >= (unsigned)g.NB) ++slot;
+  GroupStage<T, D> kst;
+  RowStage<T, D> vst;
+  if (slot < kk) {
+    const int base = tile_base(g, irow[slot]);
+    group_load<T, D>(kst, Kh, base, koff, tid);
+    row_load<T, D>(vst, Vh, base, voff, tid);
+  }
+  while (slot < kk) {
+    __syncthreads();
+    group_store<T, D>(kst, lds_kt, lds_k, tid);
+    row_store<T, D>(vst, lds_v, tid);
+    __syncthreads();
+    int nxt = slot + 1;
+    while (nxt < kk && (unsigned)irow[nxt] >= (unsigned)g.NB) ++nxt;
+    if (nxt < kk) {
+      const int base = tile_base(g, irow[nxt]);
+      group_load<T, D>(kst, Kh, base, koff, tid);
+      row_load<T, D>(vst, Vh, base, voff, tid);
+    }
+
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = f32x16{};
+      pacc[mt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        sacc[mt] = mma_step(frag_row<T, D>(lds_k, 32 * mt + l32, s, h), qf[s], sacc[mt]);
+        pacc[mt] = mma_step(frag_row<T, D>(lds_v, 32 * mt + l32, s, h), gf[s], pacc[mt]);
+      }
+    }
+    typename SplitOf<T>::type sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * (s & 1) + e;
+        const int key = 32 * (s >> 1) + 8 * (i >> 2) + 4 * h + (i & 3);
+        const float p = key < g.T ? fast_exp2(fmaf(sacc[s >> 1][i], c2, -lse2)) : 0.f;
+        sv[e] = p * (pacc[s >> 1][i] - dv);
+      }
+      to_split(sv, sf[s]);
+    }
+#pragma unroll
+    for (int t = 0; t < C::kDTiles; ++t) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dqacc[t] = mma_split_b(frag_tr<T, D>(lds_kt, 32 * t + l32, s, h), sf[s], dqacc[t]);
+    }
+    slot = nxt;
+  }
+  if (q_ok) {
+    const size_t orow = head_off + (size_t)q_tok * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int t = 0; t < C::kDTiles; ++t) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        store4(a.dQ, orow + 32 * t + 8 * gq + 4 * h, a.out_f32, sc * dqacc[t][4 * gq], sc * dqacc[t][4 * gq + 1],
+               sc * dqacc[t][4 * gq + 2], sc * dqacc[t][4 * gq + 3]);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  constexpr int CPR = D / Elem<T>::kChunkElems;
+  const size_t tokens = (size_t)a.BH * a.g.N;
+  const int tpb = 256 / CPR;
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((tokens + tpb - 1) / tpb)), dim3(256), 0, s, a);
+  const size_t nwords = (size_t)a.BH * a.g.NB * a.words;
+  const unsigned zgrid = (unsigned)((nwords + 255) / 256 < 65536 ? (nwords + 255) / 256 : 65536);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(zgrid), dim3(256), 0, s, a.bitmap, nwords);
+  const size_t nslots = (size_t)a.BH * a.g.NB * a.kmax;
+  hipLaunchKernelGGL(rev_setbits_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, a);
+  const unsigned rows4 = (unsigned)(((size_t)a.BH * a.g.NB + 3) / 4);
+  hipLaunchKernelGGL(rev_count_kernel, dim3(rows4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(rev_scan_kernel, dim3(a.BH), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(rev_fill_kernel, dim3(rows4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
+  if (io_f32) return d == 64 ? launch_bwd_t<float, 64>(a, s) : launch_bwd_t<float, 128>(a, s);
+  return d == 64 ? launch_bwd_t<bf16, 64>(a, s) : launch_bwd_t<bf16, 128>(a, s);
+}
+
+}  // namespace dsa

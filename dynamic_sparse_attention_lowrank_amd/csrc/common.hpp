@@ -1,0 +1,201 @@
+// Shared device helpers for the gfx950 (MI355X) kernels of libdsa.
+//
+// Matrix-core fragments.  Every contraction in this library is issued as a
+// sequence of 32x32 output tiles with a reduction step of 16:
+//   bf16: one v_mfma_f32_32x32x16_bf16 per step;
+//   fp32: eight v_mfma_f32_32x32x2_f32 per step (same operand registers, one
+//         element pair per instruction), so one code path serves both types.
+// Operand layout (checked on the hardware): for A (32 x 16, M x K) lane l holds
+// row l%32 and reduction elements 8*(l/32) .. 8*(l/32)+7; for B (16 x 32) lane l
+// holds column l%32 and the same 8 reduction elements.  The 32x32 fp32 result
+// gives lane l column l%32 and rows {8g + 4*(l/32) + i : g < 4, i < 4} in
+// registers 4g + i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// element-type traits
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<bf16> {
+  typedef bf16x8 frag;                 // 8 reduction elements = 16 bytes
+  static constexpr int kChunkElems = 8;  // elements per 16-byte chunk
+  static constexpr int kFragChunks = 1;  // 16-byte chunks per fragment
+};
+template <> struct Elem<f16> {
+  typedef f16x8 frag;
+  static constexpr int kChunkElems = 8;
+  static constexpr int kFragChunks = 1;
+};
+template <> struct Elem<float> {
+  typedef f32x8 frag;                  // 8 reduction elements = 32 bytes
+  static constexpr int kChunkElems = 4;
+  static constexpr int kFragChunks = 2;
+};
+
+// acc += A * B over one reduction step of 16.
+__device__ __forceinline__ f32x16 mma_step(bf16x8 a, bf16x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_step(f16x8 a, f16x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_step(f32x8 a, f32x8 b, f32x16 acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// fragment <-> raw 16-byte chunks
+__device__ __forceinline__ bf16x8 frag_from_chunks(const u32x4* c, bf16*) {
+  return __builtin_bit_cast(bf16x8, c[0]);
+}
+__device__ __forceinline__ f16x8 frag_from_chunks(const u32x4* c, f16*) {
+  return __builtin_bit_cast(f16x8, c[0]);
+}
+__device__ __forceinline__ f32x8 frag_from_chunks(const u32x4* c, float*) {
+  f32x4 lo = __builtin_bit_cast(f32x4, c[0]);
+  f32x4 hi = __builtin_bit_cast(f32x4, c[1]);
+  f32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// eight fp32 values -> fragment of the element type (round to nearest even for bf16)
+__device__ __forceinline__ bf16x8 to_frag(const float* v, bf16*) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[e];
+  return r;
+}
+__device__ __forceinline__ f16x8 to_frag(const float* v, f16*) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (f16)v[e];
+  return r;
+}
+__device__ __forceinline__ f32x8 to_frag(const float* v, float*) {
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = v[e];
+  return r;
+}
+
+// An fp32 operand computed inside a kernel (probabilities, dS) as a bf16 pair
+// hi + lo with hi = bf16(v), lo = bf16(v - hi): the pair carries about 16
+// significant bits, so contractions issued twice (hi, then lo) keep fp32-level
+// accuracy without relying on the range of any other 16-bit format.  For fp32
+// operands there is nothing to split (lo is unused).
+struct SplitBF16 {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ void to_split(const float* v, SplitBF16& s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = (bf16)v[e];
+    s.hi[e] = h;
+    s.lo[e] = (bf16)(v[e] - (float)h);
+  }
+}
+struct SplitF32 {
+  f32x8 hi;
+};
+__device__ __forceinline__ void to_split(const float* v, SplitF32& s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s.hi[e] = v[e];
+}
+template <typename T> struct SplitOf;
+template <> struct SplitOf<bf16> { typedef SplitBF16 type; };
+template <> struct SplitOf<float> { typedef SplitF32 type; };
+
+// acc += A * (hi + lo)   /   acc += (hi + lo) * B
+__device__ __forceinline__ f32x16 mma_split_b(bf16x8 a, const SplitBF16& b, f32x16 acc) {
+  acc = mma_step(a, b.hi, acc);
+  return mma_step(a, b.lo, acc);
+}
+__device__ __forceinline__ f32x16 mma_split_b(f32x8 a, const SplitF32& b, f32x16 acc) { return mma_step(a, b.hi, acc); }
+__device__ __forceinline__ f32x16 mma_split_a(const SplitBF16& a, bf16x8 b, f32x16 acc) {
+  acc = mma_step(a.hi, b, acc);
+  return mma_step(a.lo, b, acc);
+}
+__device__ __forceinline__ f32x16 mma_split_a(const SplitF32& a, f32x8 b, f32x16 acc) { return mma_step(a.hi, b, acc); }
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// ---------------------------------------------------------------------------
+// tile geometry: token offsets of the members of a tile, relative to its corner
+// ---------------------------------------------------------------------------
+struct Geo {
+  int Lt, Lh, Lw;      // latent extents
+  int tt, th, tw;      // tile extents
+  int gt, gh, gw;      // tile grid extents
+  int N, T, NB;        // tokens, tokens per tile, tiles
+};
+
+// first token of tile j (its (t, y, x) corner)
+__device__ __forceinline__ int tile_base(const Geo& g, int j) {
+  int jx = j % g.gw;
+  int jy = (j / g.gw) % g.gh;
+  int jt = j / (g.gw * g.gh);
+  return ((jt * g.tt) * g.Lh + jy * g.th) * g.Lw + jx * g.tw;
+}
+// offset of the i-th member (ascending token order) from the tile corner
+__device__ __forceinline__ int member_offset(const Geo& g, int i) {
+  int dx = i % g.tw;
+  int dy = (i / g.tw) % g.th;
+  int dt = i / (g.tw * g.th);
+  return (dt * g.Lh + dy) * g.Lw + dx;
+}
+
+// ---------------------------------------------------------------------------
+// work-group placement: consecutive hardware work-group ids are dispatched
+// round-robin over the 8 XCDs (each with its own L2).  Remap so that XCD x runs a
+// contiguous range of logical ids (same head, neighbouring tiles -> shared K/V
+// blocks stay in that XCD's L2).  A bijection on [0, G).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  constexpr int kXcd = 8;
+  int x = bid % kXcd, s = bid / kXcd;
+  int per = G / kXcd, rem = G % kXcd;
+  return x * per + (x < rem ? x : rem) + s;
+}
+
+// ---------------------------------------------------------------------------
+// wave helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// position of key kk (0..15) inside a 16-key group of a transposed operand in LDS:
+// swaps bits 2 and 3, so that the registers of a 32x32 result, read in order,
+// form the B operand of the next contraction without any lane exchange.
+__device__ __forceinline__ int perm16(int kk) {
+  return (kk & 3) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2);
+}
+
+}  // namespace dsa

@@ -1,0 +1,82 @@
+// Launch interfaces between the C-ABI layer (api.hip) and the kernel files.
+// Every launcher only enqueues work on the given stream and returns the launch
+// status; arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dsa {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const int32_t* idx;
+  const int32_t* kvec;
+  int kmax;
+  void* O;
+  float* LSE;
+  int out_f32;
+  float c;      // scale * log2(e)
+  Geo g;
+  int BH;
+};
+hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s);
+
+struct PredictArgs {
+  const void* Q;
+  const void* K;
+  const void* Wq;
+  const void* Wk;
+  float* Qbar;
+  float* Kbar;
+  float* S;
+  Geo g;
+  int B, H, r;
+};
+hipError_t launch_predict(const PredictArgs& a, int io_f32, int d, hipStream_t s);
+
+struct SelectArgs {
+  const float* S;
+  const int32_t* kvec;
+  int kmax;
+  int32_t* idx;
+  int NB;
+  int BH;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  int o_f32;            // O is float32 (else bf16)
+  const void* dO;
+  const float* LSE;
+  const int32_t* idx;
+  const int32_t* kvec;
+  int kmax;
+  float scale;
+  float c;      // scale * log2(e)
+  int out_f32;
+  void* dQ;
+  void* dK;
+  void* dV;
+  // workspace views
+  float* Dvec;          // [BH, N]
+  uint32_t* bitmap;     // [BH, NB, words]   bit tau of row j: tile tau kept block j
+  int32_t* counts;      // [BH, NB]
+  int32_t* offsets;     // [BH, NB + 1]
+  int32_t* entries;     // [BH, NB * kmax]
+  int words;            // ceil(NB / 32)
+  Geo g;
+  int BH;
+};
+hipError_t launch_attn_bwd(const BwdArgs& a, int io_f32, int d, hipStream_t s);
+
+}  // namespace dsa

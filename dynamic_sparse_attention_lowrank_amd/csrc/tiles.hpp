@@ -1,0 +1,236 @@
+// LDS staging of 64-token tiles for the attention kernels (gfx950).
+//
+// A work-group has 2 waves (128 threads); each wave owns 32 rows of a 64-row
+// operand tile.  Two LDS layouts are used for a tile of 64 tokens x D elements:
+//
+//  * row-major  [64][D]: a token row is D*sizeof(T) bytes = CPR 16-byte chunks;
+//    chunk c of row r sits at slot c ^ (r mod min(CPR,16)), so the 32 lanes that
+//    read one chunk column of 32 consecutive rows hit distinct banks;
+//  * transposed [D][64]: row d holds element d of all 64 tokens, with token
+//    position p = 16*G + perm16(k) for token 16*G + k (see common.hpp), so that
+//    one 16-byte read gives a lane the 8 tokens its MFMA operand needs.  Chunk c
+//    of row d sits at c ^ ((d ^ (d >> log2 TR)) mod TR), which keeps both the
+//    transposing writes and the operand reads spread over the banks.
+//
+// Global loads are 16-byte chunks.  A "row item" is one chunk of one token row
+// (consecutive threads take consecutive chunks of a row).  A "group item" is one
+// chunk column of the 8 tokens in one 8-position group of the transposed layout;
+// it is written both transposed and, when needed, row-major.
+#pragma once
+
+#include "common.hpp"
+
+namespace dsa {
+
+constexpr int kTileThreads = 128;
+
+template <typename T, int D>
+struct TileCfg {
+  static constexpr int kCE = Elem<T>::kChunkElems;            // elements per 16-byte chunk
+  static constexpr int kFC = Elem<T>::kFragChunks;            // chunks per MFMA fragment
+  static constexpr int kCPR = D / kCE;                        // chunks per token row
+  static constexpr int kRowPer = 64 * kCPR / kTileThreads;    // row items per thread
+  static constexpr int kGItems = 8 * kCPR;                    // group items per tile
+  static constexpr int kGPer = (kGItems + kTileThreads - 1) / kTileThreads;
+  static constexpr int kTR = 64 * (int)sizeof(T) / 16;        // chunks per transposed row
+  static constexpr int kTLog = kTR == 8 ? 3 : 4;
+  static constexpr int kRSw = kCPR < 16 ? kCPR : 16;
+  static constexpr int kSteps = D / 16;                       // reduction steps over d
+  static constexpr int kDTiles = D / 32;                      // 32-wide tiles over d
+  static constexpr int kRowChunks = 64 * kCPR;                // LDS chunks of a row-major tile
+  static constexpr int kTrChunks = D * kTR;                   // LDS chunks of a transposed tile
+};
+
+template <typename T, int D>
+__device__ __forceinline__ int row_slot(int r, int c) {
+  using C = TileCfg<T, D>;
+  return r * C::kCPR + (c ^ (r & (C::kRSw - 1)));
+}
+template <typename T, int D>
+__device__ __forceinline__ int tr_slot(int d, int c) {
+  using C = TileCfg<T, D>;
+  return d * C::kTR + (c ^ ((d ^ (d >> C::kTLog)) & (C::kTR - 1)));
+}
+// token position (0..63) stored at place e of 8-position group kg
+__device__ __forceinline__ int group_row(int kg, int e) { return 16 * (kg >> 1) + perm16(8 * (kg & 1) + e); }
+
+// --- A/B operand fragments from LDS -----------------------------------------
+// row-major tile: row r, reduction step s, lane half h -> elements 16s+8h..+7
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag frag_row(const u32x4* lds, int r, int s, int h) {
+  using C = TileCfg<T, D>;
+  u32x4 ch[C::kFC];
+#pragma unroll
+  for (int p = 0; p < C::kFC; ++p) ch[p] = lds[row_slot<T, D>(r, (2 * s + h) * C::kFC + p)];
+  return frag_from_chunks(ch, (T*)nullptr);
+}
+// transposed tile: row d, token step s (16 tokens), lane half h -> positions 16s+8h..+7
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag frag_tr(const u32x4* lds, int d, int s, int h) {
+  using C = TileCfg<T, D>;
+  u32x4 ch[C::kFC];
+#pragma unroll
+  for (int p = 0; p < C::kFC; ++p) ch[p] = lds[tr_slot<T, D>(d, (2 * s + h) * C::kFC + p)];
+  return frag_from_chunks(ch, (T*)nullptr);
+}
+// one token row straight from global memory as B operand fragments (row tok, elements 16s+8h..)
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frags(typename Elem<T>::frag* f, const T* __restrict__ row, bool ok, int h) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int s = 0; s < C::kSteps; ++s) {
+    u32x4 ch[C::kFC];
+#pragma unroll
+    for (int p = 0; p < C::kFC; ++p)
+      ch[p] = ok ? *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * h + p * C::kCE) : u32x4{0, 0, 0, 0};
+    f[s] = frag_from_chunks(ch, (T*)nullptr);
+  }
+}
+
+// --- staging: global -> registers -> LDS --------------------------------------
+// Row items: per thread kRowPer chunks; `off[i]` = token offset (relative to the
+// tile corner) of the row of item i, or -1 for a padding row.
+template <typename T, int D>
+struct RowStage {
+  u32x4 v[TileCfg<T, D>::kRowPer];
+};
+template <typename T, int D>
+__device__ __forceinline__ void row_offsets(int* off, const Geo& g, int tid) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < C::kRowPer; ++i) {
+    const int r = (tid + i * kTileThreads) / C::kCPR;
+    off[i] = r < g.T ? member_offset(g, r) : -1;
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void row_load(RowStage<T, D>& st, const T* __restrict__ X, int base, const int* off, int tid) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < C::kRowPer; ++i) {
+    const int c = (tid + i * kTileThreads) % C::kCPR;
+    st.v[i] = off[i] >= 0 ? *reinterpret_cast<const u32x4*>(X + (size_t)(base + off[i]) * D + c * C::kCE)
+                          : u32x4{0, 0, 0, 0};
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void row_store(const RowStage<T, D>& st, u32x4* lds, int tid) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < C::kRowPer; ++i) {
+    const int lc = tid + i * kTileThreads;
+    lds[row_slot<T, D>(lc / C::kCPR, lc % C::kCPR)] = st.v[i];
+  }
+}
+
+// Group items: per thread kGPer items of 8 chunks.
+template <typename T, int D>
+struct GroupStage {
+  u32x4 v[TileCfg<T, D>::kGPer][8];
+};
+template <typename T, int D>
+__device__ __forceinline__ void group_offsets(int (*off)[8], const Geo& g, int tid) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < C::kGPer; ++i) {
+    const int kg = (tid + i * kTileThreads) / C::kCPR;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = group_row(kg & 7, e);
+      off[i][e] = (kg < 8 && r < g.T) ? member_offset(g, r) : -1;
+    }
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void group_load(GroupStage<T, D>& st, const T* __restrict__ X, int base,
+                                           const int (*off)[8], int tid) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < C::kGPer; ++i) {
+    const int c = (tid + i * kTileThreads) % C::kCPR;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      st.v[i][e] = off[i][e] >= 0 ? *reinterpret_cast<const u32x4*>(X + (size_t)(base + off[i][e]) * D + c * C::kCE)
+                                  : u32x4{0, 0, 0, 0};
+  }
+}
+
+// 8 tokens x one chunk -> transposed rows.  The stored element type is the
+// source type, except that bf16 sources can be stored as fp16 (exact for values
+// in the fp16 normal range; used for the operand of the fp16 P.V product).
+__device__ __forceinline__ uint32_t bf16_half(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ void transpose_store(u32x4* lds_t, const u32x4 (&v)[8], int kg, int c, bf16*, bf16*) {
+  using C = TileCfg<bf16, 64>;  // the transposed row geometry depends only on the element size
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {            // element m of the chunk -> row d = 8c + m
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)            // positions 2j, 2j+1 of the group
+      w[j] = bf16_half(v[2 * j][m >> 1], m & 1) | (bf16_half(v[2 * j + 1][m >> 1], m & 1) << 16);
+    const int d = 8 * c + m;
+    lds_t[d * C::kTR + (kg ^ ((d ^ (d >> C::kTLog)) & (C::kTR - 1)))] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+__device__ __forceinline__ void transpose_store(u32x4* lds_t, const u32x4 (&v)[8], int kg, int c, bf16*, f16*) {
+  using C = TileCfg<f16, 64>;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16 a = (f16)bf16_bits_to_f32(bf16_half(v[2 * j][m >> 1], m & 1));
+      const f16 b = (f16)bf16_bits_to_f32(bf16_half(v[2 * j + 1][m >> 1], m & 1));
+      w[j] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+    const int d = 8 * c + m;
+    lds_t[d * C::kTR + (kg ^ ((d ^ (d >> C::kTLog)) & (C::kTR - 1)))] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+__device__ __forceinline__ void transpose_store(u32x4* lds_t, const u32x4 (&v)[8], int kg, int c, float*, float*) {
+  using C = TileCfg<float, 64>;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int d = 4 * c + m;
+    const int f = (d ^ (d >> C::kTLog)) & (C::kTR - 1);
+    lds_t[d * C::kTR + ((2 * kg) ^ f)] = u32x4{v[0][m], v[1][m], v[2][m], v[3][m]};
+    lds_t[d * C::kTR + ((2 * kg + 1) ^ f)] = u32x4{v[4][m], v[5][m], v[6][m], v[7][m]};
+  }
+}
+// store group items transposed (lds_t, element type TO) and, if lds_r != nullptr,
+// row-major too (source type T)
+template <typename T, int D, typename TO = T>
+__device__ __forceinline__ void group_store(const GroupStage<T, D>& st, u32x4* lds_t, u32x4* lds_r, int tid) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < C::kGPer; ++i) {
+    const int it = tid + i * kTileThreads;
+    if (it < C::kGItems) {
+      const int kg = it / C::kCPR, c = it % C::kCPR;
+      transpose_store(lds_t, st.v[i], kg, c, (T*)nullptr, (TO*)nullptr);
+      if (lds_r != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lds_r[row_slot<T, D>(group_row(kg, e), c)] = st.v[i][e];
+      }
+    }
+  }
+}
+
+// 4 fp32 values -> output row (16 bytes fp32, or 8 bytes bf16 rounded to nearest even)
+__device__ __forceinline__ void store4(void* base, size_t off, int out_f32, float v0, float v1, float v2, float v3) {
+  if (out_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off) = f32x4{v0, v1, v2, v3};
+  } else {
+    const bf16 b0 = (bf16)v0, b1 = (bf16)v1, b2 = (bf16)v2, b3 = (bf16)v3;
+    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16*>(base) + off) = u32x2{w0, w1};
+  }
+}
+__device__ __forceinline__ void store1(void* base, size_t off, int out_f32, float v) {
+  if (out_f32) reinterpret_cast<float*>(base)[off] = v;
+  else reinterpret_cast<bf16*>(base)[off] = (bf16)v;
+}
+
+}  // namespace dsa

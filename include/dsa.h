@@ -1,0 +1,168 @@
+/*
+ * dsa.h -- C ABI of libdsa: DSV-style dynamic block-sparse attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the DSV page (DSV: Exploiting Dynamic
+ * Sparsity to Accelerate Large-Scale Video DiT Training,
+ * gist.science/ar/paper/2502.07590): a cheap low-rank predictor guesses which
+ * small part of the attention matters (section 3a), neighbouring tokens are
+ * grouped so that one 3-D tile of queries shares one selection (section 3b), and
+ * exact attention is then computed only over what was selected (section 4,
+ * stage two), forward and backward.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Geometry.  A head holds N = Lt*Lh*Lw video tokens stored row-major over the
+ *   latent grid (t, y, x): token n = (t*Lh + y)*Lw + x.  A tile is a tt x th x tw
+ *   sub-box (tt | Lt, th | Lh, tw | Lw); tiles are numbered row-major over the
+ *   tile grid, NB = (Lt/tt)(Lh/th)(Lw/tw), T = tt*th*tw tokens per tile.  Query
+ *   tile tau and key block tau are the same tokens ("own block").  Within a tile,
+ *   tokens are taken in ascending n.
+ * Tensors.  Q, K, V, O, dO, dQ, dK, dV are dense [B, H, N, d] arrays, d
+ *   innermost, in device memory.  d is 64 or 128.  Their element type is
+ *   shape->io (DSA_BF16 or DSA_F32) unless an argument says otherwise.
+ * Empty input.  B*H == 0 is valid: the call returns DSA_OK and enqueues nothing.
+ * Limits.  N*d <= 2^31-1, B*H <= 65535, B*H*NB <= 2^31-1 (DSA_ERR_SHAPE).
+ * Ownership.  The caller owns every buffer and the stream.  The library never
+ *   allocates memory, never synchronises the device and keeps no state between
+ *   calls; each call only enqueues kernels on `stream` and returns.
+ * Errors.  All argument checks happen on the host before any HIP call; a failed
+ *   check returns its status and enqueues nothing.  A failed kernel launch
+ *   returns DSA_ERR_HIP.  Device-side values (k[], idx[]) cannot be checked by
+ *   the host without a synchronisation, so the kernels treat them defensively
+ *   (documented per entry point) and never access memory out of bounds.
+ * Determinism.  For identical inputs every entry point produces bit-identical
+ *   outputs (no floating-point atomics).
+ * Concurrency.  Calls on different streams may overlap only if their output
+ *   buffers (and workspaces) are disjoint.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define DSA_API __attribute__((visibility("default")))
+#else
+#define DSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,            /* a required pointer is NULL                        */
+  DSA_ERR_SHAPE = 2,           /* B, H, N or d out of range / unsupported          */
+  DSA_ERR_TILE = 3,            /* tile extents do not divide the latent, or T > 64 */
+  DSA_ERR_K = 4,               /* kmax out of range                                */
+  DSA_ERR_DTYPE = 5,           /* unknown element type                             */
+  DSA_ERR_WORKSPACE = 6,       /* workspace too small or misaligned                */
+  DSA_ERR_HIP = 7,             /* a HIP launch failed                              */
+  DSA_ERR_NOT_IMPLEMENTED = 8, /* combination not supported by this build          */
+  DSA_ERR_RANK = 9             /* predictor rank r out of range                    */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+
+typedef struct {
+  int32_t B, H, d;        /* batch, heads, head dimension (64 or 128)                 */
+  int32_t Lt, Lh, Lw;     /* latent extents; N = Lt*Lh*Lw                             */
+  int32_t tt, th, tw;     /* tile extents; must divide the latent; T = tt*th*tw <= 64 */
+  int32_t io;             /* dsa_dtype of Q, K, V, Wq, Wk, O (bwd input), dO          */
+} dsa_shape;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+DSA_API const char* dsa_status_string(dsa_status s);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+DSA_API int32_t dsa_version(void);
+
+/*
+ * dsa_predict -- low-rank predictor (DSV page, section 3a).
+ *   For every (b, h) and tile tau:
+ *     Qbar[b,h,tau,:] = (1/T) sum_{n in tile tau} Q[b,h,n,:] @ Wq[h]      (r values)
+ *     Kbar[b,h,tau,:] = (1/T) sum_{n in tile tau} K[b,h,n,:] @ Wk[h]
+ *     S[b,h,tau,j]    = Qbar[b,h,tau,:] . Kbar[b,h,j,:]                  (unscaled)
+ *   Q, K: [B,H,N,d] io dtype.  Wq, Wk: [H,d,r] io dtype (per-head weights).
+ *   Qbar, Kbar: outputs [B,H,NB,r] float32.  S: output [B,H,NB,NB] float32.
+ *   All arithmetic is float32 (products of the stored values, float32 sums).
+ *   r must lie in [1, 64] (DSA_ERR_RANK otherwise).
+ */
+DSA_API dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q, const void* K,
+                       const void* Wq, const void* Wk, float* Qbar, float* Kbar, float* S,
+                       hipStream_t stream);
+
+/*
+ * dsa_select -- top-k key blocks per query tile (DSV page, sections 3a-3b).
+ *   For row (b,h,tau) with k = k[b*H+h]: keep block tau itself plus the k-1 other
+ *   blocks with the largest S[b,h,tau,j]; equal scores go to the lower index
+ *   (+0 and -0 are equal; NaN ranks below every number).  The kept blocks are
+ *   written to idx[b,h,tau,0..k-1] in ascending order and idx[b,h,tau,k..kmax-1]
+ *   is set to -1.
+ *   S: [B,H,NB,NB] float32.  k: device int32 [B*H].  idx: output [B,H,NB,kmax] int32.
+ *   1 <= kmax <= NB is required (DSA_ERR_K).  A device value k outside
+ *   [1, kmax] is clamped into that range.
+ */
+DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, int32_t kmax,
+                      int32_t* idx, hipStream_t stream);
+
+/*
+ * dsa_attn_fwd -- exact softmax attention over the kept blocks (DSV page,
+ * section 4, stage two).
+ *   For each query token i of tile tau, over the keys n of the blocks
+ *   idx[b,h,tau,0..k-1]:  s_in = scale * (q_i . k_n),
+ *   O_i = sum_n softmax_n(s_in) v_n,  LSE_i = ln sum_n exp(s_in).
+ *   Q, K, V: [B,H,N,d] io dtype.  idx: [B,H,NB,kmax] int32, k: device int32 [B*H].
+ *   out_dtype: element type of O (DSA_BF16 or DSA_F32, any io).  O: [B,H,N,d].
+ *   LSE: [B,H,N] float32 (natural log).  scale is normally 1/sqrt(d).
+ *   Softmax statistics and accumulation are float32.  With bf16 io the P.V
+ *   product runs on fp16 matrix cores: V is converted to fp16 (exact for
+ *   |v| < 65504, the fp16 range; larger magnitudes overflow) and the
+ *   probabilities are rounded to fp16.
+ *   Device-side robustness: k is clamped to [1, kmax]; idx entries outside
+ *   [0, NB) are skipped; a row with no valid block gets O = 0, LSE = -inf.
+ *   Duplicate entries are the caller's responsibility (dsa_select never makes them).
+ */
+DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
+                        int32_t out_dtype, void* O, float* LSE, hipStream_t stream);
+
+/*
+ * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for
+ * this shape and kmax (0 on invalid arguments).  It holds D = rowsum(dO * O)
+ * and the reverse (key block -> query tiles) index of idx.
+ */
+DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
+
+/*
+ * dsa_attn_bwd -- gradients of the block-sparse attention with the block mask
+ * held fixed (no gradient reaches the predictor).
+ *   D_i = dO_i . O_i,  P from the forward's LSE,  dS_in = P_in (dO_i . v_n - D_i),
+ *   dQ_i = scale sum_n dS_in k_n,  dK_n = scale sum_i dS_in q_i,  dV_n = sum_i P_in dO_i.
+ *   Q, K, V, dO: [B,H,N,d] io dtype; LSE: [B,H,N] float32 from dsa_attn_fwd.
+ *   O: [B,H,N,d] forward output of element type o_dtype (DSA_F32 or DSA_BF16).
+ *   O only enters through D; its rounding enters D coherently over a whole row,
+ *   so pass the float32 forward output when gradients must match to ~1e-3.
+ *   idx, k, kmax, scale: as passed to dsa_attn_fwd.
+ *   dQ, dK, dV: outputs [B,H,N,d] of out_dtype, fully overwritten.
+ *   workspace: device memory of at least dsa_attn_bwd_workspace_bytes(shape, kmax)
+ *   bytes, 256-byte aligned; its contents on entry do not matter.
+ *   Products with the in-kernel fp32 P and dS use a bf16 hi+lo pair (two matrix-
+ *   core passes), so their accuracy does not depend on the scale of dO.
+ *   The same device-side robustness rules as dsa_attn_fwd apply.
+ */
+DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V,
+                                const void* O, int32_t o_dtype, const void* dO, const float* LSE,
+                                const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
+                                int32_t out_dtype, void* dQ, void* dK, void* dV, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/dsa.h, and rejects bad arguments on the host before any HIP
+call (these calls return before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    lib_path = os.path.join(ROOT, "dynamic_sparse_attention_lowrank_amd", "libdsa.so")
+    if not os.path.exists(lib_path):
+        from dynamic_sparse_attention_lowrank_amd import build as b
+        b.build()
+    import dynamic_sparse_attention_lowrank_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"DSA_API\s+[\w\s\*]+?\b(dsa_\w+)\s*\(", text)
+
+
+def test_header_declares_entry_points():
+    names = set(declared_functions())
+    assert {"dsa_predict", "dsa_select", "dsa_attn_fwd", "dsa_attn_bwd", "dsa_attn_bwd_workspace_bytes",
+            "dsa_status_string", "dsa_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(L.library_path)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} not exported"
+    assert L.lib.dsa_version() == 100
+
+
+def _shape(L, **kw):
+    base = dict(B=1, H=2, d=64, Lt=4, Lh=8, Lw=8, tt=1, th=4, tw=4, io=0)
+    base.update(kw)
+    return L.Shape(*[base[n] for n in ("B", "H", "d", "Lt", "Lh", "Lw", "tt", "th", "tw", "io")])
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), 2), (dict(d=0), 2), (dict(B=-1), 2), (dict(Lt=0), 2),
+    (dict(th=3), 3), (dict(tt=0), 3), (dict(tt=2, th=8, tw=8), 3),    # 128-token tile
+    (dict(io=7), 5),
+])
+def test_shape_validation(L, kw, code):
+    sh = _shape(L, **kw)
+    st = L.lib.dsa_predict(ctypes.byref(sh), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == code, L.lib.dsa_status_string(st)
+
+
+def test_entry_point_validation(L):
+    sh = _shape(L)
+    lib = L.lib
+    assert lib.dsa_predict(None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.dsa_predict(ctypes.byref(sh), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 9
+    assert lib.dsa_predict(ctypes.byref(sh), 65, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 9
+    assert lib.dsa_predict(ctypes.byref(sh), 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 0, FAKE, None) == 4
+    assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 17, FAKE, None) == 4      # kmax > NB = 16
+    assert lib.dsa_select(ctypes.byref(sh), None, FAKE, 4, FAKE, None) == 1
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, None) == 5
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, float("nan"), 0, FAKE, FAKE,
+                            None) == 2
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, None) == 1
+    need = lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 4)
+    assert need > 0
+    args = [ctypes.byref(sh)] + [FAKE] * 4 + [0] + [FAKE] * 4 + [4, 0.125, 0, FAKE, FAKE, FAKE]
+    assert lib.dsa_attn_bwd(*args, None, need, None) == 6                       # no workspace
+    assert lib.dsa_attn_bwd(*args, FAKE, need - 1, None) == 6                   # too small
+    assert lib.dsa_attn_bwd(*args, ctypes.c_void_p(0x1010), need, None) == 6    # misaligned
+    bad_o = [ctypes.byref(sh)] + [FAKE] * 4 + [2] + [FAKE] * 4 + [4, 0.125, 0, FAKE, FAKE, FAKE]
+    assert lib.dsa_attn_bwd(*bad_o, FAKE, need, None) == 5                      # unknown O dtype
+    assert lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 0) == 0
+    assert lib.dsa_attn_bwd_workspace_bytes(None, 4) == 0
+
+
+def test_empty_batch_is_a_no_op(L):
+    sh = _shape(L, B=0)
+    assert L.lib.dsa_predict(ctypes.byref(sh), 16, None, None, None, None, None, None, None, None) == 0
+    assert L.lib.dsa_attn_fwd(ctypes.byref(sh), None, None, None, None, None, 4, 0.125, 0, None, None, None) == 0
+
+
+def test_workspace_formula(L):
+    """D (fp32 per token) + bitmap (NB x ceil(NB/32) words) + counts + offsets + entries,
+    each section rounded up to 256 bytes."""
+    sh = _shape(L, B=2, H=3, d=128, Lt=3, Lh=16, Lw=24, tt=1, th=8, tw=8, io=1)
+    BH, N, NB, kmax = 6, 3 * 16 * 24, 18, 5
+    r = lambda x: (x + 255) // 256 * 256
+    want = r(BH * N * 4) + r(BH * NB * 1 * 4) + r(BH * NB * 4) + r(BH * (NB + 1) * 4) + r(BH * NB * kmax * 4)
+    assert L.lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax) == want
+
+
+def test_status_strings(L):
+    for code in range(10):
+        assert L.lib.dsa_status_string(code).startswith(b"DSA_")
