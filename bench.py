@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: one training step of DSV-style dynamic block-sparse attention on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic video tokens:
+predictor scores -> top-k block selection -> block-sparse attention forward ->
+backward (D + reverse index, dK/dV, dQ).  Workload: B=1, H=24, d=128, latent
+16x32x64 = 32,768 tokens, 1x8x8 tiles (512 blocks), rank 16, 10 % of the blocks
+kept (k = 52), bf16 inputs.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is attended TFLOP/s of the whole step with the
+attended work counted as 4*d FLOP per (query, key) pair forward and 10*d
+backward; `roofline` describes the dominant kernel, timed with HIP events on
+the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn ms/layer + attended TFLOP/s (% bf16 MFMA peak), 32,768 tok"
+BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak (published)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    csrc = os.path.join(ROOT, "dynamic_sparse_attention_lowrank_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, launches_per_step: int):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, wl, seconds: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload: heads in
+    order, each head's pooled predictor, then its query tiles in a fixed shuffled
+    order (score row, top-k selection, forward and backward of the tile) until the
+    time budget is spent (whole tiles only)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    f = lambda t: t.detach().cpu().double().numpy()
+    geom = oracle.Geometry(*wl.latent, *wl.tile)
+    mem = geom.members()
+    scale = 1.0 / math.sqrt(wl.d)
+    T = geom.T
+    order = np.random.default_rng(0).permutation(geom.NB)
+    flops, tiles, heads, busy = 0.0, 0, 0, 0.0
+    for bh in range(wl.B * wl.H):
+        b, h = divmod(bh, wl.H)
+        Q, K, V, dO = (f(x[n][b, h]) for n in ("Q", "K", "V", "dO"))      # staging, not timed
+        Wq, Wk = f(x["Wq"][h]), f(x["Wk"][h])
+        k = int(x["k"][bh])
+        t0 = time.perf_counter()
+        Qb = oracle.pooled_features(Q, Wq, mem)
+        Kb = oracle.pooled_features(K, Wk, mem)
+        heads += 1
+        for tau in order:
+            srow = oracle.block_scores(Qb[tau:tau + 1], Kb)[0]
+            blocks = list(oracle.select_row(srow, int(tau), k))
+            oracle.attn_tile(Q, K, V, mem, int(tau), blocks, scale)
+            oracle.attn_bwd_tile(Q, K, V, dO, mem, int(tau), blocks, scale)
+            flops += 14.0 * wl.d * T * (k * T)
+            tiles += 1
+            if busy + time.perf_counter() - t0 >= seconds:
+                break
+        busy += time.perf_counter() - t0
+        if busy >= seconds:
+            break
+    return {"value": flops / busy / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{wl.name}: {tiles} query tiles over {heads} head(s) of {wl.B * wl.H} "
+                      f"({geom.NB} tiles per head): per head the pooled predictor, per tile its score row, "
+                      f"top-k selection and fp64 forward + backward; {busy:.1f} s of oracle time; "
+                      f"value = counted attended FLOP (14*d per pair) of the sample / that time"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    lib_path = os.path.join(ROOT, "dynamic_sparse_attention_lowrank_amd", "libdsa.so")
+    if not os.path.exists(lib_path):
+        from dynamic_sparse_attention_lowrank_amd import build as b
+        b.build()
+    import dynamic_sparse_attention_lowrank_amd as dsa
+    from dsa_inputs import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = generate(wl, device=dev, with_grad=True)
+    lay = dsa.Layout(tuple(wl.latent), tuple(wl.tile))
+    B, H, N, d, NB, T = wl.B, wl.H, wl.N, wl.d, wl.NB, wl.T
+    kdev = x["k"].to(dev)
+    ks = x["k"].tolist()
+    kmax = int(max(ks))
+    r = wl.r
+    f32 = torch.float32
+    Qbar = torch.empty(B, H, NB, r, device=dev, dtype=f32)
+    Kbar = torch.empty_like(Qbar)
+    S = torch.empty(B, H, NB, NB, device=dev, dtype=f32)
+    idx = torch.empty(B, H, NB, kmax, device=dev, dtype=torch.int32)
+    O = torch.empty(B, H, N, d, device=dev, dtype=f32)
+    LSE = torch.empty(B, H, N, device=dev, dtype=f32)
+    dQ = torch.empty(B, H, N, d, device=dev, dtype=torch.bfloat16)
+    dK = torch.empty_like(dQ)
+    dV = torch.empty_like(dQ)
+    ws = torch.empty(dsa.bwd_workspace_bytes(x["Q"], lay, kmax), device=dev, dtype=torch.uint8)
+    Q, K, V, dO, Wq, Wk = (x[n] for n in ("Q", "K", "V", "dO", "Wq", "Wk"))
+
+    phases = ["predict", "select", "fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq"]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        dsa.predict(Q, K, Wq, Wk, lay, out=(Qbar, Kbar, S))
+        rec(1)
+        dsa.select(S, kdev, kmax, lay, d=d, out=idx)
+        rec(2)
+        dsa.attn_fwd(Q, K, V, idx, kdev, lay, out=(O, LSE))
+        rec(3)
+        dsa.attn_bwd_prepare(O, dO, idx, kdev, lay, ws)
+        rec(4)
+        dsa.attn_bwd_dkdv(Q, K, V, dO, LSE, kmax, lay, ws, dK, dV)
+        rec(5)
+        dsa.attn_bwd_dq(Q, K, V, dO, LSE, idx, kdev, lay, ws, dQ)
+        rec(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides; HIP events on the
+    # launch stream (torch's current stream) bracket every phase of every step
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    phase_ms = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
+    span_ms = events[0][0].elapsed_time(events[-1][-1]) / args.steps
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a_ = torch.empty(n, device=dev, dtype=f32)
+        b_ = torch.empty_like(a_)
+        b_.copy_(a_)
+        torch.cuda.synchronize()
+
+    pairs = sum(NB * kk * T * T for kk in ks)          # attended (query, key) pairs
+    flop_fwd = 4.0 * d * pairs
+    flop_bwd = 10.0 * d * pairs
+    flop_step = flop_fwd + flop_bwd
+    value = flop_step / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = flop_fwd / (phase_ms["fwd"] * 1e-3) / 1e12
+
+    # dominant single-kernel phase and its algorithmic work per launch
+    algo = {"fwd": (4.0 * d * pairs, "attn_fwd_kernel"),
+            "bwd_dkdv": (8.0 * d * pairs, "bwd_dkdv_kernel"),
+            "bwd_dq": (6.0 * d * pairs, "bwd_dq_kernel")}
+    dom = max(algo, key=lambda p: phase_ms[p])
+    achieved = algo[dom][0] / (phase_ms[dom] * 1e-3) / 1e12
+    traffic = load_traffic(algo[dom][1], 1)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": algo[dom][1], "ms": round(phase_ms[dom], 4),
+                "algorithmic_flop_per_launch": algo[dom][0]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: one attention layer, training step (predict+select+fwd+bwd)",
+                   "B": B, "H": H, "d": d, "latent": list(wl.latent), "tokens": N, "tile": list(wl.tile),
+                   "blocks": NB, "rank": r, "k": kmax, "keep_percent": list(wl.keep_percent)},
+        "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "fwd": {"ms": round(phase_ms["fwd"], 4), "tflops": round(fwd_tflops, 2),
+                "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2)},
+        "phase_ms": {p: round(v, 4) for p, v in phase_ms.items()},
+        "event_ms_per_step": round(span_ms, 4),
+        "counted_flop": {"fwd": flop_fwd, "bwd": flop_bwd, "pairs": pairs},
+        "roofline": roofline,
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

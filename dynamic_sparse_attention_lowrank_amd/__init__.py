@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
-    "bwd_workspace_bytes", "DsaError", "F32", "BF16",
+    "bwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
 ]
 
 F32 = 0
@@ -66,10 +66,30 @@ def _load():
     L.dsa_attn_bwd_workspace_bytes.argtypes = [sp, i32]
     L.dsa_attn_bwd.restype = ctypes.c_int
     L.dsa_attn_bwd.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+    L.dsa_attn_bwd_prepare.restype = ctypes.c_int
+    L.dsa_attn_bwd_prepare.argtypes = [sp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
+    L.dsa_attn_bwd_dkdv.restype = ctypes.c_int
+    L.dsa_attn_bwd_dkdv.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+    L.dsa_attn_bwd_dq.restype = ctypes.c_int
+    L.dsa_attn_bwd_dq.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, sz, vp]
     return L
 
 
-lib = _load()
+_lib = None
+
+
+def _L():
+    """The loaded library (loaded on first use, so the build module can run without it)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _L()
+    raise AttributeError(name)
 
 
 @dataclass(frozen=True)
@@ -126,7 +146,7 @@ def _stream() -> int:
 
 def _check(status: int) -> None:
     if status != 0:
-        raise DsaError(status, lib.dsa_status_string(status).decode())
+        raise DsaError(status, _L().dsa_status_string(status).decode())
 
 
 def predict(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, layout: Layout,
@@ -142,7 +162,7 @@ def predict(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor
         S = torch.empty(B, H, layout.NB, layout.NB, device=Q.device, dtype=torch.float32)
     else:
         Qbar, Kbar, S = out
-    _check(lib.dsa_predict(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(Qbar), _ptr(Kbar),
+    _check(_L().dsa_predict(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(Qbar), _ptr(Kbar),
                            _ptr(S), _stream()))
     return Qbar, Kbar, S
 
@@ -154,7 +174,7 @@ def select(S: torch.Tensor, k: torch.Tensor, kmax: int, layout: Layout, d: int =
     B, H = S.shape[:2]
     sh = Shape(B, H, d, *layout.latent, *layout.tile, F32)
     idx = out if out is not None else torch.empty(B, H, layout.NB, kmax, device=S.device, dtype=torch.int32)
-    _check(lib.dsa_select(ctypes.byref(sh), _ptr(S), _ptr(k), kmax, _ptr(idx), _stream()))
+    _check(_L().dsa_select(ctypes.byref(sh), _ptr(S), _ptr(k), kmax, _ptr(idx), _stream()))
     return idx
 
 
@@ -173,14 +193,14 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tenso
         LSE = torch.empty(Q.shape[:3], device=Q.device, dtype=torch.float32)
     else:
         O, LSE = out
-    _check(lib.dsa_attn_fwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
+    _check(_L().dsa_attn_fwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
                             _io_code(O), _ptr(O), _ptr(LSE), _stream()))
     return O, LSE
 
 
 def bwd_workspace_bytes(Q: torch.Tensor, layout: Layout, kmax: int) -> int:
     sh = _shape(Q, layout)
-    return int(lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
+    return int(_L().dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
 
 
 def attn_bwd(Q, K, V, O, dO, LSE, idx, k, layout: Layout, scale: Optional[float] = None,
@@ -202,11 +222,43 @@ def attn_bwd(Q, K, V, O, dO, LSE, idx, k, layout: Layout, scale: Optional[float]
         dV = torch.empty_like(dQ)
     else:
         dQ, dK, dV = out
-    need = int(lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
+    need = int(_L().dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
-    _check(lib.dsa_attn_bwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _io_code(O), _ptr(dO), _ptr(LSE),
+    _check(_L().dsa_attn_bwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _io_code(O), _ptr(dO), _ptr(LSE),
                             _ptr(idx),
                             _ptr(k), kmax, scale, _io_code(dQ), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream()))
     return dQ, dK, dV
+
+
+def _ws_args(workspace: torch.Tensor):
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def attn_bwd_prepare(O, dO, idx, k, layout: Layout, workspace: torch.Tensor) -> None:
+    """Backward phase 1: D and the reverse block index into ``workspace``."""
+    _dev(O, dO, idx, k, workspace)
+    sh = _shape(dO, layout)
+    _check(_L().dsa_attn_bwd_prepare(ctypes.byref(sh), _ptr(O), _io_code(O), _ptr(dO), _ptr(idx), _ptr(k),
+                                    idx.shape[-1], *_ws_args(workspace), _stream()))
+
+
+def attn_bwd_dkdv(Q, K, V, dO, LSE, kmax: int, layout: Layout, workspace: torch.Tensor, dK: torch.Tensor,
+                  dV: torch.Tensor, scale: Optional[float] = None) -> None:
+    """Backward phase 2: dK, dV (needs a prepared workspace)."""
+    _dev(Q, K, V, dO, LSE, workspace, dK, dV)
+    sh = _shape(Q, layout)
+    scale = 1.0 / math.sqrt(Q.shape[-1]) if scale is None else scale
+    _check(_L().dsa_attn_bwd_dkdv(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), kmax, scale,
+                                 _io_code(dK), _ptr(dK), _ptr(dV), *_ws_args(workspace), _stream()))
+
+
+def attn_bwd_dq(Q, K, V, dO, LSE, idx, k, layout: Layout, workspace: torch.Tensor, dQ: torch.Tensor,
+                scale: Optional[float] = None) -> None:
+    """Backward phase 3: dQ (needs a prepared workspace)."""
+    _dev(Q, K, V, dO, LSE, idx, k, workspace, dQ)
+    sh = _shape(Q, layout)
+    scale = 1.0 / math.sqrt(Q.shape[-1]) if scale is None else scale
+    _check(_L().dsa_attn_bwd_dq(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(idx), _ptr(k),
+                               idx.shape[-1], scale, _io_code(dQ), _ptr(dQ), *_ws_args(workspace), _stream()))

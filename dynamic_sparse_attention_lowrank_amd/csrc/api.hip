@@ -144,19 +144,26 @@ size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax) {
   return bwd_layout(dv, kmax).total;
 }
 
-dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V, const void* O,
-                        int32_t o_dtype, const void* dO, const float* LSE, const int32_t* idx, const int32_t* k, int32_t kmax,
-                        float scale, int32_t out_dtype, void* dQ, void* dK, void* dV, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+enum BwdPhase { kPrepare = 1, kDkdv = 2, kDq = 4 };
+
+// shared argument checks and workspace carving of the backward entry points
+dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const void* K, const void* V, const void* O,
+                      int32_t o_dtype, const void* dO, const float* LSE, const int32_t* idx, const int32_t* k,
+                      int32_t kmax, float scale, int32_t out_dtype, void* dQ, void* dK, void* dV, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   Derived dv;
   dsa_status st = derive(shape, &dv);
   if (st != DSA_OK) return st;
-  if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  if (o_dtype != DSA_F32 && o_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if ((phases & (kDkdv | kDq)) && out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if ((phases & kPrepare) && o_dtype != DSA_F32 && o_dtype != DSA_BF16) return DSA_ERR_DTYPE;
   if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
-  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  if ((phases & (kDkdv | kDq)) && !isfinite(scale)) return DSA_ERR_SHAPE;
   if (dv.BH == 0) return DSA_OK;
-  if (!Q || !K || !V || !O || !dO || !LSE || !idx || !k || !dQ || !dK || !dV) return DSA_ERR_NULL;
+  if ((phases & kPrepare) && (!O || !dO || !idx || !k)) return DSA_ERR_NULL;
+  if ((phases & kDkdv) && (!Q || !K || !V || !dO || !LSE || !dK || !dV)) return DSA_ERR_NULL;
+  if ((phases & kDq) && (!Q || !K || !V || !dO || !LSE || !idx || !k || !dQ)) return DSA_ERR_NULL;
   const BwdLayout l = bwd_layout(dv, kmax);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255u)) return DSA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -172,7 +179,42 @@ dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, co
   a.entries = reinterpret_cast<int32_t*>(ws + l.entries);
   a.words = l.words;
   a.g = dv.g; a.BH = dv.BH;
-  return hip_status(launch_attn_bwd(a, dv.io_f32, dv.d, stream));
+  hipError_t e = hipSuccess;
+  if (phases & kPrepare) e = launch_bwd_prepare(a, dv.io_f32, dv.d, stream);
+  if (e == hipSuccess && (phases & kDkdv)) e = launch_bwd_dkdv(a, dv.io_f32, dv.d, stream);
+  if (e == hipSuccess && (phases & kDq)) e = launch_bwd_dq(a, dv.io_f32, dv.d, stream);
+  return hip_status(e);
+}
+
+}  // namespace
+
+dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V, const void* O,
+                        int32_t o_dtype, const void* dO, const float* LSE, const int32_t* idx, const int32_t* k,
+                        int32_t kmax, float scale, int32_t out_dtype, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(kPrepare | kDkdv | kDq, shape, Q, K, V, O, o_dtype, dO, LSE, idx, k, kmax, scale, out_dtype, dQ,
+                    dK, dV, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_attn_bwd_prepare(const dsa_shape* shape, const void* O, int32_t o_dtype, const void* dO,
+                                const int32_t* idx, const int32_t* k, int32_t kmax, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(kPrepare, shape, nullptr, nullptr, nullptr, O, o_dtype, dO, nullptr, idx, k, kmax, 1.f,
+                    DSA_F32, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_attn_bwd_dkdv(const dsa_shape* shape, const void* Q, const void* K, const void* V, const void* dO,
+                             const float* LSE, int32_t kmax, float scale, int32_t out_dtype, void* dK, void* dV,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(kDkdv, shape, Q, K, V, nullptr, DSA_F32, dO, LSE, nullptr, nullptr, kmax, scale, out_dtype,
+                    nullptr, dK, dV, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_attn_bwd_dq(const dsa_shape* shape, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
+                           int32_t out_dtype, void* dQ, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(kDq, shape, Q, K, V, nullptr, DSA_F32, dO, LSE, idx, k, kmax, scale, out_dtype, dQ, nullptr,
+                    nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kTileThreads) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_prepare_t(const BwdArgs& a, hipStream_t s) {
   constexpr int CPR = D / Elem<T>::kChunkElems;
   const size_t tokens = (size_t)a.BH * a.g.N;
   const int tpb = 256 / CPR;
@@ -409,16 +409,38 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(rev_count_kernel, dim3(rows4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(rev_scan_kernel, dim3(a.BH), dim3(1024), 0, s, a);
   hipLaunchKernelGGL(rev_fill_kernel, dim3(rows4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
-  if (io_f32) return d == 64 ? launch_bwd_t<float, 64>(a, s) : launch_bwd_t<float, 128>(a, s);
-  return d == 64 ? launch_bwd_t<bf16, 64>(a, s) : launch_bwd_t<bf16, 128>(a, s);
+hipError_t launch_bwd_prepare(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
+  if (io_f32) return d == 64 ? launch_prepare_t<float, 64>(a, s) : launch_prepare_t<float, 128>(a, s);
+  return d == 64 ? launch_prepare_t<bf16, 64>(a, s) : launch_prepare_t<bf16, 128>(a, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
+  const dim3 grid(a.BH * a.g.NB), block(kTileThreads);
+  if (io_f32) {
+    if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<float, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<float, 128>), grid, block, 0, s, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 128>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
+  const dim3 grid(a.BH * a.g.NB), block(kTileThreads);
+  if (io_f32) {
+    if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<float, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<float, 128>), grid, block, 0, s, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<bf16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<bf16, 128>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dsa

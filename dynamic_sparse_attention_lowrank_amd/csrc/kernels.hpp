@@ -77,6 +77,10 @@ struct BwdArgs {
   Geo g;
   int BH;
 };
-hipError_t launch_attn_bwd(const BwdArgs& a, int io_f32, int d, hipStream_t s);
+// backward phases: prepare (D + reverse index into the workspace), then dK/dV and
+// dQ, which only read the workspace and may run in either order or concurrently
+hipError_t launch_bwd_prepare(const BwdArgs& a, int io_f32, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int io_f32, int d, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int io_f32, int d, hipStream_t s);
 
 }  // namespace dsa

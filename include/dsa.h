@@ -161,6 +161,32 @@ DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const voi
                                 int32_t out_dtype, void* dQ, void* dK, void* dV, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Backward in phases.  dsa_attn_bwd is exactly these three calls in order on one
+ * stream; callers may instead issue them separately, e.g. run dsa_attn_bwd_dkdv
+ * and dsa_attn_bwd_dq concurrently on two streams once dsa_attn_bwd_prepare has
+ * completed (both only read the workspace).  Arguments mean what they mean for
+ * dsa_attn_bwd; the workspace must be the one prepared with the same idx, k,
+ * kmax, O and dO.
+ *
+ * dsa_attn_bwd_prepare -- D = rowsum(dO * O) and the reverse index (for every
+ *   key block, the ascending list of query tiles that kept it) into the workspace.
+ * dsa_attn_bwd_dkdv    -- dK, dV: one pass per key block over the query tiles
+ *   that kept it.
+ * dsa_attn_bwd_dq      -- dQ: one pass per query tile over its kept blocks.
+ */
+DSA_API dsa_status dsa_attn_bwd_prepare(const dsa_shape* shape, const void* O, int32_t o_dtype, const void* dO,
+                                        const int32_t* idx, const int32_t* k, int32_t kmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+DSA_API dsa_status dsa_attn_bwd_dkdv(const dsa_shape* shape, const void* Q, const void* K, const void* V,
+                                     const void* dO, const float* LSE, int32_t kmax, float scale,
+                                     int32_t out_dtype, void* dK, void* dV, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+DSA_API dsa_status dsa_attn_bwd_dq(const dsa_shape* shape, const void* Q, const void* K, const void* V,
+                                   const void* dO, const float* LSE, const int32_t* idx, const int32_t* k,
+                                   int32_t kmax, float scale, int32_t out_dtype, void* dQ, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
