@@ -160,6 +160,7 @@ def main():
     dK = torch.empty_like(dQ)
     dV = torch.empty_like(dQ)
     ws = torch.empty(dsa.bwd_workspace_bytes(x["Q"], lay, kmax), device=dev, dtype=torch.uint8)
+    fws = torch.empty(dsa.fwd_workspace_bytes(x["Q"], lay), device=dev, dtype=torch.uint8)
     Q, K, V, dO, Wq, Wk = (x[n] for n in ("Q", "K", "V", "dO", "Wq", "Wk"))
 
     phases = ["predict", "select", "fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq"]
@@ -171,7 +172,7 @@ def main():
         rec(1)
         dsa.select(S, kdev, kmax, lay, d=d, out=idx)
         rec(2)
-        dsa.attn_fwd(Q, K, V, idx, kdev, lay, out=(O, LSE))
+        dsa.attn_fwd(Q, K, V, idx, kdev, lay, out=(O, LSE), workspace=fws)
         rec(3)
         dsa.attn_bwd_prepare(O, dO, idx, kdev, lay, ws)
         rec(4)

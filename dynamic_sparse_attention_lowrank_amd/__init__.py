@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
-    "bwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
+    "bwd_workspace_bytes", "fwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
 ]
 
 F32 = 0
@@ -61,7 +61,9 @@ def _load():
     L.dsa_select.restype = ctypes.c_int
     L.dsa_select.argtypes = [sp, vp, vp, i32, vp, vp]
     L.dsa_attn_fwd.restype = ctypes.c_int
-    L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp]
+    L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+    L.dsa_attn_fwd_workspace_bytes.restype = sz
+    L.dsa_attn_fwd_workspace_bytes.argtypes = [sp]
     L.dsa_attn_bwd_workspace_bytes.restype = sz
     L.dsa_attn_bwd_workspace_bytes.argtypes = [sp, i32]
     L.dsa_attn_bwd.restype = ctypes.c_int
@@ -178,9 +180,14 @@ def select(S: torch.Tensor, k: torch.Tensor, kmax: int, layout: Layout, d: int =
     return idx
 
 
+def fwd_workspace_bytes(Q: torch.Tensor, layout: Layout) -> int:
+    sh = _shape(Q, layout)
+    return int(_L().dsa_attn_fwd_workspace_bytes(ctypes.byref(sh)))
+
+
 def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, k: torch.Tensor, layout: Layout,
              scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
-             out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+             out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, workspace: Optional[torch.Tensor] = None):
     """Block-sparse attention forward: returns (O [B,H,N,d] out_dtype, LSE [B,H,N] float32)."""
     _dev(Q, K, V, idx, k)
     sh = _shape(Q, layout)
@@ -193,8 +200,12 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tenso
         LSE = torch.empty(Q.shape[:3], device=Q.device, dtype=torch.float32)
     else:
         O, LSE = out
+    if workspace is None:
+        need = int(_L().dsa_attn_fwd_workspace_bytes(ctypes.byref(sh)))
+        workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
     _check(_L().dsa_attn_fwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
-                            _io_code(O), _ptr(O), _ptr(LSE), _stream()))
+                             _io_code(O), _ptr(O), _ptr(LSE), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream()))
     return O, LSE
 
 

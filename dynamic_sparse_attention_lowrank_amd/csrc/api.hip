@@ -29,8 +29,11 @@ dsa_status derive(const dsa_shape* s, Derived* out) {
   const int64_t T = (int64_t)s->tt * s->th * s->tw;
   if (T > 64) return DSA_ERR_TILE;
   const int64_t N = (int64_t)s->Lt * s->Lh * s->Lw;
-  if (N * s->d > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  const int64_t esz = s->io == DSA_F32 ? 4 : 2;
   const int64_t NB = N / T;
+  // every per-head byte offset (token rows, and the forward's 64-position V^T
+  // blocks) must fit the kernels' signed 32-bit buffer offsets
+  if (N * s->d * esz > (int64_t)INT32_MAX || NB * s->d * 64 * esz > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
   const int64_t BH = (int64_t)s->B * s->H;
   if (BH > 65535 || BH * NB > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
   Geo g;
@@ -118,9 +121,15 @@ dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, 
   return hip_status(launch_select(a, stream));
 }
 
+size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape) {
+  Derived dv;
+  if (derive(shape, &dv) != DSA_OK) return 0;
+  return attn_fwd_workspace_bytes(dv.BH, dv.g.NB, dv.d, dv.io_f32);
+}
+
 dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, const void* V, const int32_t* idx,
                         const int32_t* k, int32_t kmax, float scale, int32_t out_dtype, void* O, float* LSE,
-                        hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Derived dv;
   dsa_status st = derive(shape, &dv);
   if (st != DSA_OK) return st;
@@ -129,10 +138,13 @@ dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, co
   if (!isfinite(scale)) return DSA_ERR_SHAPE;
   if (dv.BH == 0) return DSA_OK;
   if (!Q || !K || !V || !idx || !k || !O || !LSE) return DSA_ERR_NULL;
+  const size_t need = attn_fwd_workspace_bytes(dv.BH, dv.g.NB, dv.d, dv.io_f32);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return DSA_ERR_WORKSPACE;
   FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.idx = idx; a.kvec = k; a.kmax = kmax;
   a.O = O; a.LSE = LSE; a.out_f32 = out_dtype == DSA_F32;
   a.c = scale * kLog2e;
+  a.Vt = workspace;
   a.g = dv.g; a.BH = dv.BH;
   return hip_status(launch_attn_fwd(a, dv.io_f32, dv.d, stream));
 }

@@ -22,9 +22,11 @@ struct FwdArgs {
   float* LSE;
   int out_f32;
   float c;      // scale * log2(e)
+  void* Vt;     // workspace: per block, V transposed to [d][64 key positions]
   Geo g;
   int BH;
 };
+size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32);
 hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s);
 
 struct PredictArgs {

@@ -22,7 +22,8 @@
  *   innermost, in device memory.  d is 64 or 128.  Their element type is
  *   shape->io (DSA_BF16 or DSA_F32) unless an argument says otherwise.
  * Empty input.  B*H == 0 is valid: the call returns DSA_OK and enqueues nothing.
- * Limits.  N*d <= 2^31-1, B*H <= 65535, B*H*NB <= 2^31-1 (DSA_ERR_SHAPE).
+ * Limits.  N*d*esize and NB*d*64*esize below 2^31 bytes (esize = 2 for bf16, 4 for
+ *   fp32), B*H <= 65535, B*H*NB <= 2^31-1 (DSA_ERR_SHAPE).
  * Ownership.  The caller owns every buffer and the stream.  The library never
  *   allocates memory, never synchronises the device and keeps no state between
  *   calls; each call only enqueues kernels on `stream` and returns.
@@ -111,6 +112,13 @@ DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int3
                       int32_t* idx, hipStream_t stream);
 
 /*
+ * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
+ * this shape (0 on invalid arguments): B*H*NB*d*64 elements of fp16 (bf16 io)
+ * or fp32 (fp32 io).  It receives every key block's V, transposed.
+ */
+DSA_API size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape);
+
+/*
  * dsa_attn_fwd -- exact softmax attention over the kept blocks (DSV page,
  * section 4, stage two).
  *   For each query token i of tile tau, over the keys n of the blocks
@@ -119,6 +127,8 @@ DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int3
  *   Q, K, V: [B,H,N,d] io dtype.  idx: [B,H,NB,kmax] int32, k: device int32 [B*H].
  *   out_dtype: element type of O (DSA_BF16 or DSA_F32, any io).  O: [B,H,N,d].
  *   LSE: [B,H,N] float32 (natural log).  scale is normally 1/sqrt(d).
+ *   workspace: device memory of at least dsa_attn_fwd_workspace_bytes(shape)
+ *   bytes, 256-byte aligned; contents on entry do not matter (DSA_ERR_WORKSPACE).
  *   Softmax statistics and accumulation are float32.  With bf16 io the P.V
  *   product runs on fp16 matrix cores: V is converted to fp16 (exact for
  *   |v| < 65504, the fp16 range; larger magnitudes overflow) and the
@@ -128,8 +138,9 @@ DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int3
  *   Duplicate entries are the caller's responsibility (dsa_select never makes them).
  */
 DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, const void* V,
-                        const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
-                        int32_t out_dtype, void* O, float* LSE, hipStream_t stream);
+                                const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
+                                int32_t out_dtype, void* O, float* LSE, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for

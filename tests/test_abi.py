@@ -69,10 +69,17 @@ def test_entry_point_validation(L):
     assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 0, FAKE, None) == 4
     assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 17, FAKE, None) == 4      # kmax > NB = 16
     assert lib.dsa_select(ctypes.byref(sh), None, FAKE, 4, FAKE, None) == 1
-    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, None) == 5
+    fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
+    assert fneed == 1 * 2 * 16 * 64 * 64 * 4                                    # B*H*NB*d*64 fp32
+    fw = [FAKE, fneed, None]
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, *fw) == 5
     assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, float("nan"), 0, FAKE, FAKE,
-                            None) == 2
-    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, None) == 1
+                            *fw) == 2
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, *fw) == 1
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, None, fneed,
+                            None) == 6
+    assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, FAKE,
+                            fneed - 1, None) == 6
     need = lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 4)
     assert need > 0
     args = [ctypes.byref(sh)] + [FAKE] * 4 + [0] + [FAKE] * 4 + [4, 0.125, 0, FAKE, FAKE, FAKE]
@@ -88,7 +95,8 @@ def test_entry_point_validation(L):
 def test_empty_batch_is_a_no_op(L):
     sh = _shape(L, B=0)
     assert L.lib.dsa_predict(ctypes.byref(sh), 16, None, None, None, None, None, None, None, None) == 0
-    assert L.lib.dsa_attn_fwd(ctypes.byref(sh), None, None, None, None, None, 4, 0.125, 0, None, None, None) == 0
+    assert L.lib.dsa_attn_fwd(ctypes.byref(sh), None, None, None, None, None, 4, 0.125, 0, None, None, None, 0,
+                              None) == 0
 
 
 def test_workspace_formula(L):
