@@ -6,26 +6,30 @@
 // section 3b: one selection per tile of neighbouring queries).
 //
 // Two kernels:
-//  1. vt_prep: every key block's V rows, transposed to [d][64 key positions] (key
-//     positions in perm16 order, padding keys zero) and, for bf16 inputs,
-//     converted to fp16.  One HBM pass; afterwards a block's V^T is 16 KB of
-//     contiguous memory from which MFMA A fragments load directly.  Each block
-//     is gathered by ~k query tiles, so transposing once replaces k transposes.
-//  2. attn_fwd: one work-group (2 waves) per query tile of T <= 64 tokens.  Wave
-//     w takes key positions 32w..32w+31 of every kept block for all 64 query
-//     rows, so each wave loads only its half of K and V^T, straight from L2 into
-//     registers (no LDS staging), double-buffered one block ahead:
-//        S^T (32 keys x 64 queries) = K Q^T          16 MFMA, Q in registers
+//  1. kv_prep: one pass over K and V that writes every key block in fragment-
+//     major order into the caller's workspace: K as MFMA A fragments of S^T = K Q^T,
+//     V transposed (and, for bf16 inputs, converted to fp16) as A fragments of
+//     O^T = V^T P^T.  Each fragment is 64 lanes x 16 B contiguous, so every load
+//     of the attention kernel reads 1 KB contiguous (8 full cache lines) instead
+//     of 32 B from each of 32 rows.  A block is gathered by ~k query tiles, so one
+//     reorganisation serves all of them.
+//  2. attn_fwd: one work-group (2 waves) per query tile of T <= 64 tokens, two
+//     waves per SIMD (<= 256 registers): while one wave runs its softmax the other
+//     keeps the matrix cores busy.  Wave w takes key positions 32w..32w+31 of every
+//     kept block for all 64 query rows:
+//        S^T (32 keys x 64 queries) = K Q^T          16 MFMA; Q tile in LDS,
+//                                                    fragments read one step ahead
 //        online softmax (fp32, base 2), one query per lane and N-tile
-//        O^T (d x 64 queries)      += V^T P^T        16 MFMA, P^T taken straight
+//        O^T (d x 64 queries)      += V^T P^T        16 MFMA; P^T taken straight
 //                                                    from the S^T registers
-//     Each wave keeps its own running max / sum / O over its key half; the two
-//     halves are merged once, through LDS, at the end.
+//     K(j+1) is requested as soon as S(j) has consumed K(j), V(j+1) as soon as the
+//     P.V product has consumed V(j).  Each wave keeps its own running max / sum /
+//     O over its key half; the halves are merged once, through LDS, at the end.
 // With bf16 inputs the P.V product runs on fp16 matrix cores (V converted in
-// vt_prep, exact for |v| < 65504; P rounded to fp16, 2^-12 relative).  The
-// running maximum only moves when a row's maximum grows by more than 2^8, so
-// most blocks skip rescaling O; this is exact (numerator and denominator share
-// the maximum).
+// kv_prep, exact for |v| < 65504; P rounded to fp16, 2^-12 relative) and the row
+// sum adds the same fp16 probabilities (v_dot2, fp32 accumulation).  The running
+// maximum only moves when a row's maximum grows by more than 2^8, so most blocks
+// skip rescaling O; this is exact (numerator and denominator share the maximum).
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -39,40 +43,68 @@ template <typename T> struct PVType;
 template <> struct PVType<bf16> { typedef f16 type; };
 template <> struct PVType<float> { typedef float type; };
 
-// ------------------------------------------------------------ 1. V -> V^T blocks
-// One work-group of 256 threads per (head, block): rows in (coalesced 16-byte
-// chunks) -> LDS [64][D] fp32 -> out as [D][64] rows of the P.V element type.
+// ------------------------------------------------------------ 1. K, V -> fragment-major blocks
+// Output per (head, block j), for each 32-key half w: the K A-fragments of the
+// d/16 reduction steps, then the V^T A-fragments of the (d/32) x 2 (d tile, key
+// step) pairs.  A fragment is 64 lanes x 16 bytes stored lane-major, so one load
+// instruction of the attention kernel reads 1 KB contiguous.
+//  * K fragment chunk (w, f, lane) = 16-byte input chunk (d0 / CE) of key row
+//    32w + lane%32 with d0 = 16*(f/FC) + 8*(lane/32) + CE*(f%FC): a permutation of
+//    chunks, no transposition.
+//  * V^T fragment chunk (w, f=(t*2+s)*PFC+p, lane) holds element d = 32t + lane%32
+//    of the keys at positions 32w + 16s + 8*(lane/32) + PE*p + e (key via perm16):
+//    a thread transposes a CE x CE block (CE keys x CE elements) in registers,
+//    converting to the P.V element type.
+// One work-group of 256 threads per (head, block); all global accesses are
+// 16-byte chunks.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void vt_prep_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256) void kv_prep_kernel(FwdArgs a) {
   typedef typename PVType<T>::type PT;
-  constexpr int CE = Elem<T>::kChunkElems;
+  constexpr int CE = Elem<T>::kChunkElems;                     // == Elem<PT>::kChunkElems
   constexpr int CPR = D / CE;
-  __shared__ float tile[64][D + 1];
+  constexpr int FC = Elem<T>::kFragChunks;
+  constexpr int KF = D / 16 * FC;                              // K chunks per lane per half
+  constexpr int PFC = Elem<PT>::kFragChunks;
+  static_assert(Elem<PT>::kChunkElems == CE, "square register transpose");
   const Geo g = a.g;
-  const int bj = blockIdx.x;                 // bh * NB + j
+  const int bj = blockIdx.x;
   const int bh = bj / g.NB, j = bj - bh * g.NB;
-  const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + (size_t)bh * g.N * D;
+  const size_t hoff = (size_t)bh * g.N * D;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(a.K) + hoff;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + hoff;
   const int base = tile_base(g, j);
-  for (int it = threadIdx.x; it < 64 * CPR; it += 256) {
-    const int r = it / CPR, c = it % CPR;                  // r: key (member) index
-    float v[CE];
-    if (r < g.T) {
-      const u32x4 ch = *reinterpret_cast<const u32x4*>(Vh + (size_t)(base + member_offset(g, r)) * D + c * CE);
-      const T* e = reinterpret_cast<const T*>(&ch);
-#pragma unroll
-      for (int q = 0; q < CE; ++q) v[q] = to_f32(e[q]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < CE; ++q) v[q] = 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < CE; ++q) tile[r][c * CE + q] = v[q];
+  u32x4* __restrict__ ko = reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.Kf) + (size_t)bj * 64 * D);
+  u32x4* __restrict__ vo = reinterpret_cast<u32x4*>(reinterpret_cast<PT*>(a.Vt) + (size_t)bj * 64 * D);
+  // K: 2 * KF * 64 output chunks
+  for (int it = threadIdx.x; it < 2 * KF * 64; it += 256) {
+    const int lane = it % 64, f = (it / 64) % KF, w = it / (64 * KF);
+    const int r = 32 * w + (lane & 31);
+    const int d0 = 16 * (f / FC) + 8 * (lane >> 5) + CE * (f % FC);
+    ko[it] = r < g.T ? *reinterpret_cast<const u32x4*>(Kh + (size_t)(base + member_offset(g, r)) * D + d0)
+                     : u32x4{0, 0, 0, 0};
   }
-  __syncthreads();
-  PT* __restrict__ out = reinterpret_cast<PT*>(a.Vt) + (size_t)bj * D * 64;
-  for (int it = threadIdx.x; it < D * 64; it += 256) {
-    const int d = it >> 6, p = it & 63;                    // position p holds key 16*(p/16) + perm16(p%16)
-    out[it] = (PT)tile[16 * (p >> 4) + perm16(p & 15)][d];
+  // V: (64 / CE) position groups x CPR chunk columns, one CE x CE block each
+  for (int it = threadIdx.x; it < (64 / CE) * CPR; it += 256) {
+    const int c = it % CPR, pg = it / CPR;                     // chunk column, position group
+    u32x4 in[CE];
+#pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      const int pos = CE * pg + e;
+      const int key = 16 * (pos >> 4) + perm16(pos & 15);
+      in[e] = key < g.T ? *reinterpret_cast<const u32x4*>(Vh + (size_t)(base + member_offset(g, key)) * D + c * CE)
+                        : u32x4{0, 0, 0, 0};
+    }
+    const int w = (CE * pg) / 32, s2 = ((CE * pg) % 32) / 16, hh = ((CE * pg) % 16) / 8, p = ((CE * pg) % 8) / CE;
+#pragma unroll
+    for (int m = 0; m < CE; ++m) {                             // element m of the chunks -> d row c*CE + m
+      const int d = c * CE + m;
+      PT e[CE];
+#pragma unroll
+      for (int q = 0; q < CE; ++q) e[q] = (PT)to_f32(reinterpret_cast<const T*>(&in[q])[m]);
+      const int t = d / 32, lane = (d % 32) + 32 * hh;
+      const int f = (t * 2 + s2) * PFC + p;
+      vo[(w * (D / 32 * 2 * PFC) + f) * 64 + lane] = *reinterpret_cast<const u32x4*>(e);
+    }
   }
 }
 
@@ -107,33 +139,32 @@ struct VFrags {
   typename Elem<typename FwdCfg<T, D>::PT>::frag f[FwdCfg<T, D>::kDTiles][2];
 };
 
-// kvoff: lane byte offset of (key row, element 8h) inside a tile; ksoff: the tile's first row
+// Fragment-major blocks: fragment f of half w of block j starts at
+// ((j*2 + w)*F + f) * 1 KB; lane l reads bytes 16l..16l+15.
 template <typename T, int D>
-__device__ __forceinline__ void load_k(KFrags<T, D>& kf, __amdgpu_buffer_rsrc_t rk, int kvoff, int ksoff) {
+__device__ __forceinline__ void load_k(KFrags<T, D>& kf, __amdgpu_buffer_rsrc_t rk, int lvoff, int soff) {
   using C = FwdCfg<T, D>;
-  constexpr int CE = Elem<T>::kChunkElems, FC = Elem<T>::kFragChunks;
+  constexpr int FC = Elem<T>::kFragChunks;
 #pragma unroll
   for (int s = 0; s < C::kSteps; ++s) {
     u32x4 ch[FC];
 #pragma unroll
-    for (int q = 0; q < FC; ++q) ch[q] = bload(rk, kvoff + (16 * s + q * CE) * (int)sizeof(T), ksoff);
+    for (int q = 0; q < FC; ++q) ch[q] = bload(rk, lvoff + (s * FC + q) * 1024, soff);
     kf.f[s] = frag_from_chunks(ch, (T*)nullptr);
   }
 }
-// vvoff: lane byte offset of (row l32, position 32w + 8h) inside a block's V^T; vsoff: the block
 template <typename T, int D>
-__device__ __forceinline__ void load_v(VFrags<T, D>& vf, __amdgpu_buffer_rsrc_t rv, int vvoff, int vsoff) {
+__device__ __forceinline__ void load_v(VFrags<T, D>& vf, __amdgpu_buffer_rsrc_t rv, int lvoff, int soff) {
   using C = FwdCfg<T, D>;
   typedef typename C::PT PT;
-  constexpr int PE = Elem<PT>::kChunkElems, PFC = Elem<PT>::kFragChunks;
+  constexpr int PFC = Elem<PT>::kFragChunks;
 #pragma unroll
   for (int t = 0; t < C::kDTiles; ++t) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 ch[PFC];
 #pragma unroll
-      for (int q = 0; q < PFC; ++q)
-        ch[q] = bload(rv, vvoff + (16 * s + q * PE) * (int)sizeof(PT), vsoff + 32 * t * 64 * (int)sizeof(PT));
+      for (int q = 0; q < PFC; ++q) ch[q] = bload(rv, lvoff + ((t * 2 + s) * PFC + q) * 1024, soff);
       vf.f[t][s] = frag_from_chunks(ch, (PT*)nullptr);
     }
   }
@@ -145,21 +176,53 @@ struct WaveState {
   float m[2], l[2];                      // running max (log2 units) and lane-partial sum per N-tile
 };
 
+// row sum of eight probabilities as the P.V product sees them (fp16: the same
+// rounded values as the numerator, summed exactly in fp32 by v_dot2)
+__device__ __forceinline__ float frag_sum(const f16x8& p, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2(h2{p[e], p[e + 1]}, one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const f32x8& p, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc += p[e];
+  return acc;
+}
+
+// S^T for one block: A = K rows (registers), B = Q rows (LDS, row-major tile)
 template <typename T, int D>
-__device__ __forceinline__ void attend_block(WaveState<T, D>& st, const KFrags<T, D>& kf, const VFrags<T, D>& vf,
-                                             const typename Elem<T>::frag (*qf)[FwdCfg<T, D>::kSteps],
-                                             float c2, int kvalid, int h) {
+__device__ __forceinline__ void block_scores(f32x16 (&s)[2], const KFrags<T, D>& kf, const u32x4* lds_q, int l32, int h) {
+  using C = FwdCfg<T, D>;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) s[nt] = f32x16{};
+  // Q fragments are read one step ahead of the MFMAs that use them
+  typedef typename Elem<T>::frag Frag;
+  Frag qa0 = frag_row<T, D>(lds_q, l32, 0, h), qa1 = frag_row<T, D>(lds_q, 32 + l32, 0, h);
+#pragma unroll
+  for (int k = 0; k < C::kSteps; ++k) {
+    Frag qb0 = qa0, qb1 = qa1;
+    if (k + 1 < C::kSteps) {
+      qb0 = frag_row<T, D>(lds_q, l32, k + 1, h);
+      qb1 = frag_row<T, D>(lds_q, 32 + l32, k + 1, h);
+    }
+    s[0] = mma_step(kf.f[k], qa0, s[0]);
+    s[1] = mma_step(kf.f[k], qa1, s[1]);
+    qa0 = qb0;
+    qa1 = qb1;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// online softmax of one block's scores; returns the P^T fragments (B operand of the P.V product)
+template <typename T, int D, bool FULL>
+__device__ __forceinline__ void block_softmax(WaveState<T, D>& st, f32x16 (&s)[2],
+                                              typename Elem<typename FwdCfg<T, D>::PT>::frag (&pf)[2][2],
+                                              float c2, int kvalid, int h) {
   using C = FwdCfg<T, D>;
   typedef typename C::PT PT;
-  typedef typename Elem<PT>::frag PFrag;
-  f32x16 s[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    s[nt] = f32x16{};
-#pragma unroll
-    for (int k = 0; k < C::kSteps; ++k) s[nt] = mma_step(kf.f[k], qf[nt][k], s[nt]);
-  }
-  if (kvalid < 32) {                        // padding keys of this wave's half (T < 64 only)
+  if constexpr (!FULL) {                      // padding keys of this wave's half (T < 64)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
@@ -167,13 +230,13 @@ __device__ __forceinline__ void attend_block(WaveState<T, D>& st, const KFrags<T
         if (8 * (i >> 2) + 4 * h + (i & 3) >= kvalid) s[nt][i] = -INFINITY;
     }
   }
-  PFrag pf[2][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float mb = s[nt][0];
+    float mb = fmaxf(fmaxf(s[nt][0], s[nt][1]), s[nt][2]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mb = fmaxf(mb, s[nt][i]);
-    mb = fmaxf(mb, xor32(mb));
+    for (int i = 3; i < 15; i += 2) mb = fmaxf(fmaxf(mb, s[nt][i]), s[nt][i + 1]);
+    mb = fmaxf(mb, s[nt][15]);
+    mb = pair_max(mb);
     const float mnew = mb * c2;
     if (ballot(mnew > st.m[nt] + kRescaleSlack)) {
       const float mt = fmaxf(st.m[nt], mnew);
@@ -188,14 +251,17 @@ __device__ __forceinline__ void attend_block(WaveState<T, D>& st, const KFrags<T
     for (int ks = 0; ks < 2; ++ks) {
       float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(s[nt][8 * ks + e], c2, mneg));
-        st.l[nt] += p;
-        pv[e] = p;
-      }
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(s[nt][8 * ks + e], c2, mneg));
       pf[nt][ks] = to_frag(pv, (PT*)nullptr);
+      st.l[nt] = frag_sum(pf[nt][ks], st.l[nt]);
     }
   }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void block_pv(WaveState<T, D>& st, const VFrags<T, D>& vf,
+                                         const typename Elem<typename FwdCfg<T, D>::PT>::frag (&pf)[2][2]) {
+  using C = FwdCfg<T, D>;
 #pragma unroll
   for (int t = 0; t < C::kDTiles; ++t) {
 #pragma unroll
@@ -206,13 +272,22 @@ __device__ __forceinline__ void attend_block(WaveState<T, D>& st, const KFrags<T
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kTileThreads) void attn_fwd_kernel(FwdArgs a) {
+// Two waves per SIMD (<= 256 registers each): while one wave runs its softmax
+// the other keeps the matrix cores busy.
+template <typename T, int D, bool FULL>
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, D>;
-  typedef typename Elem<T>::frag Frag;
-  // merge buffer: per wave, the partial of the query N-tile the other wave stores
-  __shared__ float mrg_o[2][C::kDTiles * 16][64];
-  __shared__ float mrg_ml[2][2][64];
+  typedef typename C::PT PT;
+  typedef typename Elem<PT>::frag PFrag;
+  using TC = TileCfg<T, D>;
+  // the Q tile (row-major, swizzled) during the block loop; the merge buffers after it
+  constexpr int kQBytes = TC::kRowChunks * 16;
+  constexpr int kMrgBytes = (2 * C::kDTiles * 16 * 64 + 2 * 2 * 64) * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kQBytes > kMrgBytes ? kQBytes : kMrgBytes];
+  u32x4* lds_q = reinterpret_cast<u32x4*>(smem);
+  float (*mrg_o)[C::kDTiles * 16][64] = reinterpret_cast<float (*)[C::kDTiles * 16][64]>(smem);
+  float (*mrg_ml)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + 2 * C::kDTiles * 16 * 64 * 4);
 
   const Geo g = a.g;
   const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
@@ -229,16 +304,16 @@ __global__ __launch_bounds__(kTileThreads) void attn_fwd_kernel(FwdArgs a) {
   kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
   const int tau_base = tile_base(g, tau);
 
-  // queries: N-tile nt holds rows 32nt .. 32nt+31
-  Frag qf[2][C::kSteps];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int q = 32 * nt + l32;
-    const bool ok = q < g.T;
-    load_row_frags<T, D>(qf[nt], Qh + (size_t)(tau_base + (ok ? member_offset(g, q) : 0)) * D, ok, h);
+  {  // stage the Q tile once
+    int qoff[TC::kRowPer];
+    row_offsets<T, D>(qoff, g, tid);
+    RowStage<T, D> qs;
+    row_load<T, D>(qs, Qh, tau_base, qoff, tid);
+    row_store<T, D>(qs, lds_q, tid);
   }
-  // this lane's key row inside the wave's half of a block
-  const int kr = 32 * w + l32;
+  __syncthreads();
+
+  const int kr = 32 * w + l32;                // this lane's key row inside the wave's half
   const bool k_ok = kr < g.T;
   const int koff = k_ok ? member_offset(g, kr) : 0;
   const int kvalid = g.T - 32 * w;            // valid keys in this wave's half (may be <= 0)
@@ -253,62 +328,56 @@ __global__ __launch_bounds__(kTileThreads) void attn_fwd_kernel(FwdArgs a) {
   }
 
   if (kvalid > 0) {
-    typedef typename C::PT PT;
     const float c2 = a.c;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (size_t)g.N * D * sizeof(T));
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(reinterpret_cast<const PT*>(a.Vt) + (size_t)bh * g.NB * D * 64, (size_t)g.NB * D * 64 * sizeof(PT));
-    const int kvoff = (koff * D + 8 * h) * (int)sizeof(T);
-    const int vvoff = (l32 * 64 + 32 * w + 8 * h) * (int)sizeof(PT);
-    const int vblk = D * 64 * (int)sizeof(PT);
-    // K of the next block is fetched one block ahead (ping-pong k0/k1); V of the
-    // current block is fetched at its start and lands during S^T and the softmax.
-    KFrags<T, D> k0, k1;
+    const size_t hblk = (size_t)g.NB * 64 * D;   // elements per head in the fragment-major copies
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.Kf) + (size_t)bh * hblk, hblk * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const PT*>(a.Vt) + (size_t)bh * hblk, hblk * sizeof(PT));
+    const int kblk = 64 * D * (int)sizeof(T), vblk = 64 * D * (int)sizeof(PT);
+    const int klv = w * (kblk / 2) + lane * 16, vlv = w * (vblk / 2) + lane * 16;
+    // One register buffer for both operands: V(j) is requested once S(j) has
+    // consumed K(j), K(j+1) once the P.V product has consumed V(j).  The second
+    // wave on the SIMD covers the load latency.  Invalid idx entries are skipped.
+    KFrags<T, D> kf;
     VFrags<T, D> vf;
-    int j = irow[0];
-    bool v0 = (unsigned)j < (unsigned)g.NB;
-    if (v0) load_k<T, D>(k0, rk, kvoff, tile_base(g, j) * D * (int)sizeof(T));
-    for (int slot = 0; slot < kk; slot += 2) {
-      bool v1 = false;
-      int j1 = 0;
-      if (slot + 1 < kk) {
-        j1 = irow[slot + 1];
-        v1 = (unsigned)j1 < (unsigned)g.NB;
-        if (v1) load_k<T, D>(k1, rk, kvoff, tile_base(g, j1) * D * (int)sizeof(T));
-      }
-      if (v0) {
-        load_v<T, D>(vf, rv, vvoff, j * vblk);
-        attend_block<T, D>(st, k0, vf, qf, c2, kvalid, h);
-      }
-      if (slot + 1 >= kk) break;
-      v0 = false;
-      if (slot + 2 < kk) {
-        j = irow[slot + 2];
-        v0 = (unsigned)j < (unsigned)g.NB;
-        if (v0) load_k<T, D>(k0, rk, kvoff, tile_base(g, j) * D * (int)sizeof(T));
-      }
-      if (v1) {
-        load_v<T, D>(vf, rv, vvoff, j1 * vblk);
-        attend_block<T, D>(st, k1, vf, qf, c2, kvalid, h);
-      }
+    int slot = 0;
+    while (slot < kk && (unsigned)irow[slot] >= (unsigned)g.NB) ++slot;
+    if (slot < kk) {
+      load_k<T, D>(kf, rk, klv, irow[slot] * kblk);
+      load_v<T, D>(vf, rv, vlv, irow[slot] * vblk);
+    }
+    while (slot < kk) {
+      int nxt = slot + 1;
+      while (nxt < kk && (unsigned)irow[nxt] >= (unsigned)g.NB) ++nxt;
+      f32x16 s[2];
+      block_scores<T, D>(s, kf, lds_q, l32, h);
+      if (nxt < kk) load_k<T, D>(kf, rk, klv, irow[nxt] * kblk);        // K(j+1) behind S(j)
+      PFrag pf[2][2];
+      block_softmax<T, D, FULL>(st, s, pf, c2, kvalid, h);
+      block_pv<T, D>(st, vf, pf);
+      if (nxt < kk) load_v<T, D>(vf, rv, vlv, irow[nxt] * vblk);        // V(j+1) behind P.V(j)
+      slot = nxt;
     }
   }
+  __syncthreads();                            // Q no longer read: reuse its LDS for the merge
 
-  // ---- merge the two key halves: wave w stores N-tile w, hands N-tile 1-w over
-  const int give = 1 - w;
+  // ---- merge the two key halves: wave w stores N-tile w and hands N-tile 1-w
+  // over through LDS (compile-time register indices only, selected per wave)
+  const bool w1 = w != 0;
 #pragma unroll
   for (int t = 0; t < C::kDTiles; ++t) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mrg_o[w][t * 16 + i][lane] = st.o[give][t][i];
+    for (int i = 0; i < 16; ++i) mrg_o[w][t * 16 + i][lane] = w1 ? st.o[0][t][i] : st.o[1][t][i];
   }
-  mrg_ml[w][0][lane] = st.m[give];
-  mrg_ml[w][1][lane] = st.l[give];
+  mrg_ml[w][0][lane] = w1 ? st.m[0] : st.m[1];
+  mrg_ml[w][1][lane] = w1 ? st.l[0] : st.l[1];
   __syncthreads();
   const int other = 1 - w;
-  const float ma = st.m[w], mb = mrg_ml[other][0][lane];
-  const float la = st.l[w] + xor32(st.l[w]);
+  const float ma = w1 ? st.m[1] : st.m[0];
+  const float la0 = w1 ? st.l[1] : st.l[0];
+  const float la = pair_sum(la0);
+  const float mb = mrg_ml[other][0][lane];
   const float lb0 = mrg_ml[other][1][lane];
-  const float lb = lb0 + __shfl_xor(lb0, 32, 64);
+  const float lb = pair_sum(lb0);
   const float mt = fmaxf(ma, mb);
   const float wa = (ma == -INFINITY) ? 0.f : fast_exp2(ma - mt);
   const float wb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - mt);
@@ -326,7 +395,8 @@ __global__ __launch_bounds__(kTileThreads) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * gq + i;
-          v[i] = (wa * st.o[w][t][r] + wb * mrg_o[other][t * 16 + r][lane]) * inv;
+          const float own = w1 ? st.o[1][t][r] : st.o[0][t][r];
+          v[i] = (wa * own + wb * mrg_o[other][t * 16 + r][lane]) * inv;
         }
         store4(a.O, orow + 32 * t + 8 * gq + 4 * h, a.out_f32, v[0], v[1], v[2], v[3]);
       }
@@ -336,16 +406,20 @@ __global__ __launch_bounds__(kTileThreads) void attn_fwd_kernel(FwdArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((vt_prep_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
+hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
+  FwdArgs a = a0;
+  a.Kf = a0.Vt;
+  a.Vt = reinterpret_cast<char*>(a0.Vt) + (size_t)a0.BH * a0.g.NB * 64 * D * sizeof(T);
+  hipLaunchKernelGGL((kv_prep_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
+  if (a.g.T == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32) {
-  return (size_t)BH * NB * d * 64 * (io_f32 ? 4 : 2);
+  return 2 * (size_t)BH * NB * d * 64 * (io_f32 ? 4 : 2);      // K and V^T, fragment-major
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s) {

@@ -23,6 +23,7 @@ struct FwdArgs {
   int out_f32;
   float c;      // scale * log2(e)
   void* Vt;     // workspace: per block, V transposed to [d][64 key positions]
+  void* Kf;     // workspace: per block, K in fragment order (when used)
   Geo g;
   int BH;
 };

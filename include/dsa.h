@@ -113,8 +113,10 @@ DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int3
 
 /*
  * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
- * this shape (0 on invalid arguments): B*H*NB*d*64 elements of fp16 (bf16 io)
- * or fp32 (fp32 io).  It receives every key block's V, transposed.
+ * this shape (0 on invalid arguments): 2*B*H*NB*d*64 elements of 2 bytes (bf16
+ * io) or 4 bytes (fp32 io).  dsa_attn_fwd first rewrites every key block's K
+ * and V (V transposed; fp16 for bf16 io) there in the order its matrix-core
+ * fragments are loaded.
  */
 DSA_API size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape);
 

@@ -70,7 +70,7 @@ def test_entry_point_validation(L):
     assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 17, FAKE, None) == 4      # kmax > NB = 16
     assert lib.dsa_select(ctypes.byref(sh), None, FAKE, 4, FAKE, None) == 1
     fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
-    assert fneed == 1 * 2 * 16 * 64 * 64 * 4                                    # B*H*NB*d*64 fp32
+    assert fneed == 2 * (1 * 2 * 16 * 64 * 64 * 4)                              # K and V^T: 2*B*H*NB*d*64 fp32
     fw = [FAKE, fneed, None]
     assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, *fw) == 5
     assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, float("nan"), 0, FAKE, FAKE,
