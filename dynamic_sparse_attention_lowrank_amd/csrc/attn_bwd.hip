@@ -159,14 +159,22 @@ __global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 3. dK, dV
+// One work-group (2 waves) per key block; wave w owns keys 32w..32w+31, whose K and
+// V rows stay in registers as the B operands of S = Q K^T and dP = dO V^T.  For
+// each query tile that kept the block (ascending CSC list) the Q and dO rows and
+// the tile's LSE and D are staged once in LDS (shared by both waves; the next
+// tile's rows are fetched into registers while the current one is computed):
+//   S, dP  (64 queries x 32 keys)   A = Q / dO rows (ds_read_b128)
+//   P = exp2(S*c - LSE*log2e), dS = P (dP - D)      lane = key column
+//   dV += P^T dO, dK += dS^T Q      A = P^T / dS^T straight from the S registers
+//                                   (bf16 hi+lo pairs), B = dO / Q read
+//                                   transposed from the same LDS rows
 template <typename T, int D>
 __global__ __launch_bounds__(kTileThreads) void bwd_dkdv_kernel(BwdArgs a) {
   using C = TileCfg<T, D>;
   typedef typename Elem<T>::frag Frag;
   __shared__ u32x4 lds_q[C::kRowChunks];
-  __shared__ u32x4 lds_qt[C::kTrChunks];
   __shared__ u32x4 lds_g[C::kRowChunks];
-  __shared__ u32x4 lds_gt[C::kTrChunks];
   __shared__ float lds_lse[64];
   __shared__ float lds_dv[64];
 
@@ -175,50 +183,58 @@ __global__ __launch_bounds__(kTileThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int bh = L / g.NB;
   const int j = L - bh * g.NB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5, i16 = lane & 15;
   const size_t head_off = (size_t)bh * g.N * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(a.Q) + head_off;
   const T* __restrict__ Gh = reinterpret_cast<const T*>(a.dO) + head_off;
   const int jbase = tile_base(g, j);
 
-  // this lane's key row as B fragments (S = Q K^T, dP = dO V^T: N = keys)
-  const int kr = 32 * wave + l32;
+  // this lane's key row (B fragments of S = Q K^T and dP = dO V^T: N = keys)
+  const int kr = 32 * w + l32;
   const bool k_ok = kr < g.T;
   const int k_tok = jbase + (k_ok ? member_offset(g, kr) : 0);
   Frag kf[C::kSteps], vf[C::kSteps];
   load_row_frags<T, D>(kf, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, h);
   load_row_frags<T, D>(vf, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, h);
 
-  int goff[C::kGPer][8];
-  group_offsets<T, D>(goff, g, tid);
-  int qmo = -1;                                   // member offset of query row tid (tid < 64)
-  if (tid < 64 && tid < g.T) qmo = member_offset(g, tid);
+  int qoff[C::kRowPer];
+  row_offsets<T, D>(qoff, g, tid);
+  const int qmo = (tid < 64 && tid < g.T) ? member_offset(g, tid) : -1;   // query row tid (stats)
 
-  f32x16 dkacc[C::kDTiles], dvacc[C::kDTiles];
+  f32x16 dk[C::kDTiles], dv[C::kDTiles];
 #pragma unroll
   for (int t = 0; t < C::kDTiles; ++t) {
-    dkacc[t] = f32x16{};
-    dvacc[t] = f32x16{};
+    dk[t] = f32x16{};
+    dv[t] = f32x16{};
   }
   const float c2 = a.c;
   const int* list = a.entries + (size_t)bh * g.NB * a.kmax;
   const int* off = a.offsets + (size_t)bh * (g.NB + 1);
   const int e0 = off[j], e1 = off[j + 1];
 
-  GroupStage<T, D> qst, gst;
-  for (int e = e0; e < e1; ++e) {
-    const int tau = list[e];
+  RowStage<T, D> qs, gs;
+  float lse_r = 0.f, d_r = 0.f;
+  auto fetch = [&](int tau) {
     const int base = tile_base(g, tau);
-    group_load<T, D>(qst, Qh, base, goff, tid);
-    group_load<T, D>(gst, Gh, base, goff, tid);
-    group_store<T, D>(qst, lds_qt, lds_q, tid);     // the previous pass ended with a barrier
-    group_store<T, D>(gst, lds_gt, lds_g, tid);
+    row_load<T, D>(qs, Qh, base, qoff, tid);
+    row_load<T, D>(gs, Gh, base, qoff, tid);
     if (tid < 64) {
       const size_t t_idx = (size_t)bh * g.N + base + (qmo >= 0 ? qmo : 0);
-      lds_lse[tid] = qmo >= 0 ? a.LSE[t_idx] * kLog2e : INFINITY;
-      lds_dv[tid] = qmo >= 0 ? a.Dvec[t_idx] : 0.f;
+      lse_r = qmo >= 0 ? a.LSE[t_idx] * kLog2e : INFINITY;     // padding rows: P = 0
+      d_r = qmo >= 0 ? a.Dvec[t_idx] : 0.f;
+    }
+  };
+  if (e0 < e1) fetch(list[e0]);
+  for (int e = e0; e < e1; ++e) {
+    __syncthreads();                           // previous tile no longer read
+    row_store<T, D>(qs, lds_q, tid);
+    row_store<T, D>(gs, lds_g, tid);
+    if (tid < 64) {
+      lds_lse[tid] = lse_r;
+      lds_dv[tid] = d_r;
     }
     __syncthreads();
+    if (e + 1 < e1) fetch(list[e + 1]);
 
     f32x16 sacc[2], pacc[2];
 #pragma unroll
@@ -237,49 +253,51 @@ __global__ __launch_bounds__(kTileThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int q0 = 32 * mt + 8 * gq + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[q0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dv[q0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(sacc[mt][4 * gq + i], c2, -lds_lse[q0 + i]));
+          const float p = fast_exp2(fmaf(sacc[mt][4 * gq + i], c2, -l4[i]));
           sacc[mt][4 * gq + i] = p;
-          pacc[mt][4 * gq + i] = p * (pacc[mt][4 * gq + i] - lds_dv[q0 + i]);
+          pacc[mt][4 * gq + i] = p * (pacc[mt][4 * gq + i] - d4[i]);
         }
       }
     }
     typename SplitOf<T>::type pf[4], sf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int ks = 0; ks < 4; ++ks) {
       float pv[8], sv[8];
 #pragma unroll
       for (int e2 = 0; e2 < 8; ++e2) {
-        pv[e2] = sacc[s >> 1][8 * (s & 1) + e2];
-        sv[e2] = pacc[s >> 1][8 * (s & 1) + e2];
+        pv[e2] = sacc[ks >> 1][8 * (ks & 1) + e2];
+        sv[e2] = pacc[ks >> 1][8 * (ks & 1) + e2];
       }
-      to_split(pv, pf[s]);
-      to_split(sv, sf[s]);
+      to_split(pv, pf[ks]);
+      to_split(sv, sf[ks]);
     }
 #pragma unroll
     for (int t = 0; t < C::kDTiles; ++t) {
+      const int col0 = 32 * t + 16 * (l32 >> 4);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        dvacc[t] = mma_split_a(pf[s], frag_tr<T, D>(lds_gt, 32 * t + l32, s, h), dvacc[t]);
-        dkacc[t] = mma_split_a(sf[s], frag_tr<T, D>(lds_qt, 32 * t + l32, s, h), dkacc[t]);
+      for (int ks = 0; ks < 4; ++ks) {
+        dv[t] = mma_split_a(pf[ks], frag_tr_rows<T, D>(lds_g, col0, ks, h, i16, (T*)nullptr), dv[t]);
+        dk[t] = mma_split_a(sf[ks], frag_tr_rows<T, D>(lds_q, col0, ks, h, i16, (T*)nullptr), dk[t]);
       }
     }
-    __syncthreads();
   }
 
-  // store: lane holds d column 32t + l32, key rows 32*wave + 8g + 4h + i
+  // store: lane holds d column 32t + l32, key rows 32w + 8g + 4h + i
 #pragma unroll
   for (int gq = 0; gq < 4; ++gq) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 32 * wave + 8 * gq + 4 * h + i;
+      const int r = 32 * w + 8 * gq + 4 * h + i;
       if (r < g.T) {
         const size_t orow = head_off + (size_t)(jbase + member_offset(g, r)) * D;
 #pragma unroll
         for (int t = 0; t < C::kDTiles; ++t) {
-          store1(a.dK, orow + 32 * t + l32, a.out_f32, a.scale * dkacc[t][4 * gq + i]);
-          store1(a.dV, orow + 32 * t + l32, a.out_f32, dvacc[t][4 * gq + i]);
+          store1(a.dK, orow + 32 * t + l32, a.out_f32, a.scale * dk[t][4 * gq + i]);
+          store1(a.dV, orow + 32 * t + l32, a.out_f32, dv[t][4 * gq + i]);
         }
       }
     }

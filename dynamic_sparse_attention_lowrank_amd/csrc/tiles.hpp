@@ -87,6 +87,40 @@ __device__ __forceinline__ void load_row_frags(typename Elem<T>::frag* f, const 
   }
 }
 
+// Transposed operand fragment from a row-major tile whose rows are the reduction
+// index (e.g. queries): lane l gets column col0 + l%16 (col0 = 32t + 16*((l%32)/16))
+// and the 8 rows {16s+4h+0..3, 16s+8+4h+0..3} -- the perm16 order in which the
+// P^T / dS^T fragments taken from a 32x32 result hold their reduction index.
+// 16-bit types use gfx950's transposing LDS read (ds_read_b64_tr_b16): within
+// each 16-lane group, lane j points at row r0 + j/4, columns col0 + 4*(j%4)..+3,
+// and lane i receives column col0 + i of rows r0..r0+3.  fp32 reads element-wise.
+template <typename T, int D>
+__device__ __forceinline__ bf16x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, bf16*) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int col = col0 + 4 * (i & 3);
+  const int chunk = col >> 3, byte = (col & 7) * 2;
+  const int r1 = 16 * s + 4 * h + (i >> 2), r2 = r1 + 8;
+  const char* base = reinterpret_cast<const char*>(lds);
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r1, chunk) * 16 + byte));
+  const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r2, chunk) * 16 + byte));
+  return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+}
+template <typename T, int D>
+__device__ __forceinline__ f32x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, float*) {
+  const int col = col0 + i;
+  const int chunk = col >> 2, within = col & 3;
+  const float* base = reinterpret_cast<const float*>(lds);
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = 16 * s + (e < 4 ? 4 * h + e : 8 + 4 * h + e - 4);
+    r[e] = base[row_slot<T, D>(row, chunk) * 4 + within];
+  }
+  return r;
+}
+
 // --- staging: global -> registers -> LDS --------------------------------------
 // Row items: per thread kRowPer chunks; `off[i]` = token offset (relative to the
 // tile corner) of the row of item i, or -1 for a padding row.
