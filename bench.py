@@ -41,7 +41,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run one device-to-device copy of this size (HBM counter calibration)")
+                    help="after timing, run one int32 bitwise-not of this many MiB (a plain streaming "
+                         "kernel of known traffic, the HBM counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 output under DIR and exit "
+                         "(DIR/trace, DIR/fetch, DIR/write, each with the bench JSON line in out.json "
+                         "and the command in cmd.txt)")
     return ap.parse_args()
 
 
@@ -55,10 +60,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, launches_per_step: int):
+def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
     taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -123,6 +128,9 @@ def cpu_baseline(x, wl, seconds: float):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -199,9 +207,9 @@ def main():
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
-        a_ = torch.empty(n, device=dev, dtype=f32)
+        a_ = torch.zeros(n, device=dev, dtype=torch.int32)
         b_ = torch.empty_like(a_)
-        b_.copy_(a_)
+        torch.bitwise_not(a_, out=b_)                   # reads n*4 bytes, writes n*4 bytes
         torch.cuda.synchronize()
 
     pairs = sum(NB * kk * T * T for kk in ks)          # attended (query, key) pairs
@@ -217,7 +225,7 @@ def main():
             "bwd_dq": (6.0 * d * pairs, "bwd_dq_kernel")}
     dom = max(algo, key=lambda p: phase_ms[p])
     achieved = algo[dom][0] / (phase_ms[dom] * 1e-3) / 1e12
-    traffic = load_traffic(algo[dom][1], 1)
+    traffic = load_traffic(algo[dom][1], wl.name)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": algo[dom][1], "ms": round(phase_ms[dom], 4),
@@ -251,6 +259,140 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> profiles/ summaries
+
+def _kernel_label(raw: str) -> str:
+    """Short name of a library kernel from its (mangled or demangled) symbol."""
+    import re
+    m = re.search(r"([a-z][a-z0-9_]*_kernel)", raw)
+    if not m:
+        return raw[:60]
+    name = m.group(1)
+    tail = raw[m.end():]
+    args = []
+    if tail.startswith("I") or tail.startswith("<"):
+        if "DF16b" in tail[:8] or "__bf16" in tail[:12]:
+            args.append("bf16")
+        elif tail.startswith("If") or tail.startswith("<float"):
+            args.append("fp32")
+        d = re.match(r"I(?:DF16b|f)?(?:Li(\d+)E)+", tail) or re.match(r"<[^,>]*, (\d+)", tail)
+        if d:
+            args.append(d.group(1))
+        s = re.match(r"ILi(\d+)EE", tail) or re.match(r"<(\d+)>", tail)
+        if s and not args:
+            args.append(s.group(1))
+        if "Lb1E" in tail[:30] or "true>" in tail[:30]:
+            args.append("full")
+    return f"{name}<{','.join(args)}>" if args else name
+
+
+def _is_library_kernel(raw: str) -> bool:
+    return "dsa" in raw and "_kernel" in raw
+
+
+def _read_run(sub: str):
+    cmd = open(os.path.join(sub, "cmd.txt")).read().strip()
+    out = None
+    for line in open(os.path.join(sub, "out.json")):
+        line = line.strip()
+        if line.startswith("{"):
+            out = json.loads(line)
+    return cmd, out
+
+
+def _counter_rows(sub: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(sub, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize(root: str):
+    """Write profiles/<workload>_kernel_trace.md from a `--kernel-trace --stats` run
+    and profiles/traffic_<kernel>_<workload>.txt from one FETCH_SIZE and one
+    WRITE_SIZE `--pmc` run, each counter scaled by what it reads for the
+    calibration kernel (an int32 bitwise-not over --copy-probe-mib MiB: exactly
+    that many bytes read and written)."""
+    import csv
+    import glob
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+
+    cmd, out = _read_run(os.path.join(root, "trace"))
+    wl_name = out["config"]["workload"].split(":")[0]
+    stats = glob.glob(os.path.join(root, "trace", "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = [r for r in csv.DictReader(open(stats)) if _is_library_kernel(r["Name"])]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    c = out["config"]
+    lines = [f"# Kernel trace: {wl_name} training step (B={c['B']} H={c['H']} d={c['d']}, {c['tokens']:,} tokens, "
+             f"tile {'x'.join(map(str, c['tile']))}, k={c['k']}, bf16)", "",
+             "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
+             f"Library sources: source_hash {out['source_hash']} (bench.py prints the same hash).", "",
+             f"Library kernels only ({out['warmup']} warm-up + {out['steps']} timed steps per kernel); "
+             "the other rows of the raw summary are torch's input generator.", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "In-bench HIP-event phase times of the same run, ms:", "",
+              "    " + json.dumps(out["phase_ms"]), "",
+              f"Step {out['ms_per_step']} ms, {out['value']} attended TFLOP/s; forward {out['fwd']['ms']} ms = "
+              f"{out['fwd']['tflops']} TFLOP/s (the profiler's serialisation inflates the step slightly)."]
+    with open(os.path.join(prof, f"{wl_name}_kernel_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    per = {}
+    cmds = {}
+    probe = {}
+    hashes = set()
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        cmds[counter], o = _read_run(os.path.join(root, sub))
+        hashes.add(o["source_hash"])
+        mib = None
+        import re
+        m = re.search(r"--copy-probe-mib (\d+)", cmds[counter])
+        if m:
+            mib = int(m.group(1))
+        rows = _counter_rows(os.path.join(root, sub), counter)
+        cal = [v for n, v in rows if "bitwise_not" in n]
+        probe[counter] = (mib, max(cal) if cal else None)
+        for n, v in rows:
+            if _is_library_kernel(n):
+                per.setdefault(_kernel_label(n), {}).setdefault(counter, []).append(v)
+    if len(hashes) != 1:
+        raise SystemExit(f"counter runs come from different sources: {hashes}")
+    src_hash = hashes.pop()
+    for label, cs in per.items():
+        if "FETCH_SIZE" not in cs or "WRITE_SIZE" not in cs:
+            continue
+        kname = label.split("<")[0]
+        body = [f"# HBM traffic per launch of {label} on {wl_name}, from rocprofv3 counters", "#",
+                f"# fetch command: {cmds['FETCH_SIZE']}", f"# write command: {cmds['WRITE_SIZE']}", "#",
+                "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by bytes / counter reading of the",
+                "# calibration kernel (int32 bitwise-not over the probe size: reads and writes exactly that many bytes).",
+                f"kernel: {label}", f"workload: {wl_name}"]
+        tot = 0.0
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = cs[counter]
+            avg = sum(v) / len(v)
+            mib, cal = probe[counter]
+            scale = (mib * (1 << 20)) / (cal * 1024.0) if (mib and cal) else 1.0
+            key = counter.split("_")[0].lower()
+            body += [f"{key}_dispatches: {len(v)}", f"{key}_kib_per_dispatch: {avg:.1f}",
+                     f"{key}_probe_kib: {cal if cal is not None else 'none'}", f"{key}_scale: {scale:.4f}",
+                     f"{key}_bytes_per_launch: {avg * 1024.0 * scale:.0f}"]
+            tot += avg * 1024.0 * scale
+        body += [f"hbm_bytes_per_launch: {tot:.0f}", f"source_hash: {src_hash}"]
+        with open(os.path.join(prof, f"traffic_{kname}_{wl_name}.txt"), "w") as fh:
+            fh.write("\n".join(body) + "\n")
+    print(f"wrote profiles for {wl_name} (source_hash {src_hash}); current sources {source_hash()}")
 
 
 if __name__ == "__main__":
