@@ -58,6 +58,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < CE; ++e) s = fmaf(ov[e], to_f32(gv[e]), s);
+    if constexpr (sizeof(T) == 2) {            // fp16 copy of dO for the fp16 products of the backward
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) h[e] = (f16)to_f32(gv[e]);
+      *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.dO16) + tok * D + c * CE) = h;
+    }
   }
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
@@ -159,146 +165,192 @@ __global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 3. dK, dV
-// One work-group (2 waves) per key block; wave w owns keys 32w..32w+31, whose K and
-// V rows stay in registers as the B operands of S = Q K^T and dP = dO V^T.  For
-// each query tile that kept the block (ascending CSC list) the Q and dO rows and
-// the tile's LSE and D are staged once in LDS (shared by both waves; the next
-// tile's rows are fetched into registers while the current one is computed):
-//   S, dP  (64 queries x 32 keys)   A = Q / dO rows (ds_read_b128)
-//   P = exp2(S*c - LSE*log2e), dS = P (dP - D)      lane = key column
-//   dV += P^T dO, dK += dS^T Q      A = P^T / dS^T straight from the S registers
-//                                   (bf16 hi+lo pairs), B = dO / Q read
-//                                   transposed from the same LDS rows
-template <typename T, int D>
-__global__ __launch_bounds__(kTileThreads) void bwd_dkdv_kernel(BwdArgs a) {
+// Operand types: with bf16 inputs the products that take P or dO (dP = dO V^T,
+// dV = P^T dO) run on fp16 matrix cores (dO from the fp16 copy written by the
+// prepare phase, V converted when loaded, P in [0,1] rounded to fp16); S = Q K^T
+// and dK = dS^T Q stay bf16, dS as a hi+lo pair.  fp32 inputs use fp32 throughout.
+template <typename T> struct GradType;
+template <> struct GradType<bf16> { typedef f16 type; };
+template <> struct GradType<float> { typedef float type; };
+
+__device__ __forceinline__ f16x8 to_grad_frag(bf16x8 v, f16*) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (f16)(float)v[e];
+  return r;
+}
+__device__ __forceinline__ f32x8 to_grad_frag(f32x8 v, float*) { return v; }
+
+// One work-group of 4 waves per key block, two waves per SIMD (<= 256 registers);
+// wave w owns keys 16w..16w+15, whose K and V rows stay in registers as the B
+// operands of the 16x16x32 products S = Q K^T and dP = dO V^T.  The query tiles of
+// the block's CSC list stream through two LDS buffers (Q, dO, LSE and D of one
+// tile each), filled by direct global->LDS loads (no register staging): tile e+1
+// is requested before tile e is computed.  Per tile and wave:
+//   S, dP  (64 queries x 16 keys)  A = Q / dO rows (ds_read_b128), 4 x 4 MFMA each
+//   P = exp2(S c - LSE log2 e), dS = P (dP - D)     lane = key column
+//   dV += P^T dO, dK += dS^T Q     A = P^T / dS^T straight from the S / dP registers
+//                                  (the k-slots follow the result's row order),
+//                                  B = dO / Q read transposed (ds_read_b64_tr_b16)
+template <typename T, int D, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  typedef typename GradType<T>::type G;
+  constexpr int W = 4;
   using C = TileCfg<T, D>;
+  using CG = TileCfg<G, D>;
   typedef typename Elem<T>::frag Frag;
-  __shared__ u32x4 lds_q[C::kRowChunks];
-  __shared__ u32x4 lds_g[C::kRowChunks];
-  __shared__ float lds_lse[64];
-  __shared__ float lds_dv[64];
+  typedef typename Elem<G>::frag GFrag;
+  typedef typename SplitOf<T>::type Split;
+  constexpr int KS = D / 32;                  // 32-wide reduction steps over d
+  constexpr int DT = D / 16;                  // 16-wide output tiles over d
+  __shared__ u32x4 q0[C::kRowChunks], q1[C::kRowChunks];
+  __shared__ u32x4 g0[CG::kRowChunks], g1[CG::kRowChunks];
+  __shared__ float st0[2][64], st1[2][64];    // [LSE, D][query row]
 
   const Geo g = a.g;
   const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
   const int bh = L / g.NB;
   const int j = L - bh * g.NB;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5, i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
   const size_t head_off = (size_t)bh * g.N * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(a.Q) + head_off;
-  const T* __restrict__ Gh = reinterpret_cast<const T*>(a.dO) + head_off;
+  const G* __restrict__ Gh = (__is_same(G, T) ? reinterpret_cast<const G*>(a.dO)
+                                               : reinterpret_cast<const G*>(a.dO16)) + head_off;
+  const float* __restrict__ LSEh = a.LSE + (size_t)bh * g.N;
+  const float* __restrict__ Dh = a.Dvec + (size_t)bh * g.N;
   const int jbase = tile_base(g, j);
 
-  // this lane's key row (B fragments of S = Q K^T and dP = dO V^T: N = keys)
-  const int kr = 32 * w + l32;
+  // this lane's key row: B fragments of S = Q K^T and dP = dO V^T (N = keys)
+  const int kr = 16 * w + l16;
   const bool k_ok = kr < g.T;
   const int k_tok = jbase + (k_ok ? member_offset(g, kr) : 0);
-  Frag kf[C::kSteps], vf[C::kSteps];
-  load_row_frags<T, D>(kf, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, h);
-  load_row_frags<T, D>(vf, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, h);
-
-  int qoff[C::kRowPer];
-  row_offsets<T, D>(qoff, g, tid);
-  const int qmo = (tid < 64 && tid < g.T) ? member_offset(g, tid) : -1;   // query row tid (stats)
-
-  f32x16 dk[C::kDTiles], dv[C::kDTiles];
+  Frag kf[KS];
+  GFrag vf[KS];
+  load_row_frags16<T, D>(kf, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, q);
+  {
+    Frag vt[KS];
+    load_row_frags16<T, D>(vt, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, q);
 #pragma unroll
-  for (int t = 0; t < C::kDTiles; ++t) {
-    dk[t] = f32x16{};
-    dv[t] = f32x16{};
+    for (int s = 0; s < KS; ++s) vf[s] = to_grad_frag(vt[s], (G*)nullptr);
+  }
+
+  int qoff[DmaCfg<T, D, W>::kPer], goff[DmaCfg<G, D, W>::kPer];
+  dma_offsets<T, D, W>(qoff, g, w, lane);
+  dma_offsets<G, D, W>(goff, g, w, lane);
+  const int soff = lane < g.T ? member_offset(g, lane) : 0;   // stats row of lane (waves 0, 1)
+
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    dk[t] = f32x4{};
+    dv[t] = f32x4{};
   }
   const float c2 = a.c;
   const int* list = a.entries + (size_t)bh * g.NB * a.kmax;
   const int* off = a.offsets + (size_t)bh * (g.NB + 1);
-  const int e0 = off[j], e1 = off[j + 1];
+  const int e0 = off[j], n = off[j + 1] - e0;
 
-  RowStage<T, D> qs, gs;
-  float lse_r = 0.f, d_r = 0.f;
-  auto fetch = [&](int tau) {
+  // 16-bit tiles: closed-form operand addresses (one lane constant each)
+  constexpr bool kFast = sizeof(T) == 2;
+  const int rowl = row_lane16<D>(l16, q), trl = tr_lane16<D>(l16, q);
+
+  auto request = [&](int tau, u32x4* lq, u32x4* lg, float (*lst)[64]) {
     const int base = tile_base(g, tau);
-    row_load<T, D>(qs, Qh, base, qoff, tid);
-    row_load<T, D>(gs, Gh, base, qoff, tid);
-    if (tid < 64) {
-      const size_t t_idx = (size_t)bh * g.N + base + (qmo >= 0 ? qmo : 0);
-      lse_r = qmo >= 0 ? a.LSE[t_idx] * kLog2e : INFINITY;     // padding rows: P = 0
-      d_r = qmo >= 0 ? a.Dvec[t_idx] : 0.f;
-    }
+    dma_tile<T, D, W>(lq, Qh + (size_t)base * D, qoff, w);
+    dma_tile<G, D, W>(lg, Gh + (size_t)base * D, goff, w);
+    if (w < 2) dma_row_stats(lst[w], (w == 0 ? LSEh : Dh) + base, soff);
   };
-  if (e0 < e1) fetch(list[e0]);
-  for (int e = e0; e < e1; ++e) {
-    __syncthreads();                           // previous tile no longer read
-    row_store<T, D>(qs, lds_q, tid);
-    row_store<T, D>(gs, lds_g, tid);
-    if (tid < 64) {
-      lds_lse[tid] = lse_r;
-      lds_dv[tid] = d_r;
-    }
-    __syncthreads();
-    if (e + 1 < e1) fetch(list[e + 1]);
-
-    f32x16 sacc[2], pacc[2];
+  auto compute = [&](const u32x4* lq, const u32x4* lg, const float (*lst)[64]) {
+    // S and dP: lane holds key column kr, query rows 16mt + 4q + i
+    f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x16{};
-      pacc[mt] = f32x16{};
+    for (int mt = 0; mt < 4; ++mt) {
+      sacc[mt] = f32x4{};
+      pacc[mt] = f32x4{};
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        sacc[mt] = mma_step(frag_row<T, D>(lds_q, 32 * mt + l32, s, h), kf[s], sacc[mt]);
-        pacc[mt] = mma_step(frag_row<T, D>(lds_g, 32 * mt + l32, s, h), vf[s], pacc[mt]);
-      }
-    }
-    // P and dS; lane holds key column kr, query rows 32mt + 8g + 4h + i
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int q0 = 32 * mt + 8 * gq + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[q0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dv[q0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(sacc[mt][4 * gq + i], c2, -l4[i]));
-          sacc[mt][4 * gq + i] = p;
-          pacc[mt][4 * gq + i] = p * (pacc[mt][4 * gq + i] - d4[i]);
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (kFast) {
+          const int xs = rowl ^ (64 * s);
+          sacc[mt] = mma16(frag16_row_fast<T, D>(lq, mt, xs), kf[s], sacc[mt]);
+          pacc[mt] = mma16(frag16_row_fast<G, D>(lg, mt, xs), vf[s], pacc[mt]);
+        } else {
+          sacc[mt] = mma16(frag16_row<T, D>(lq, 16 * mt + l16, s, q), kf[s], sacc[mt]);
+          pacc[mt] = mma16(frag16_row<G, D>(lg, 16 * mt + l16, s, q), vf[s], pacc[mt]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);      // bounds the operand reads in flight
     }
-    typename SplitOf<T>::type pf[4], sf[4];
+    // P and dS as A operands: k-slot e of step ks <-> query 32ks + 16(e/4) + 4q + e%4
+    GFrag pf[2];
+    Split sf[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       float pv[8], sv[8];
 #pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        pv[e2] = sacc[ks >> 1][8 * (ks & 1) + e2];
-        sv[e2] = pacc[ks >> 1][8 * (ks & 1) + e2];
+      for (int hf = 0; hf < 2; ++hf) {
+        const int mt = 2 * ks + hf, r0 = 16 * mt + 4 * q;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lst[0][r0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lst[1][r0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = fast_exp2(fmaf(sacc[mt][i], c2, -l4[i] * kLog2e));
+          if constexpr (!FULL) p = (r0 + i < g.T) ? p : 0.f;      // padding query rows
+          pv[4 * hf + i] = p;
+          sv[4 * hf + i] = p * (pacc[mt][i] - d4[i]);
+        }
       }
-      to_split(pv, pf[ks]);
+      pf[ks] = to_frag(pv, (G*)nullptr);
       to_split(sv, sf[ks]);
     }
+    // dV += P^T dO, dK += dS^T Q: lane holds d column 16t + l16, key rows 4q + i
 #pragma unroll
-    for (int t = 0; t < C::kDTiles; ++t) {
-      const int col0 = 32 * t + 16 * (l32 >> 4);
+    for (int t = 0; t < DT; ++t) {
+      const int xt = trl ^ (32 * t);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        dv[t] = mma_split_a(pf[ks], frag_tr_rows<T, D>(lds_g, col0, ks, h, i16, (T*)nullptr), dv[t]);
-        dk[t] = mma_split_a(sf[ks], frag_tr_rows<T, D>(lds_q, col0, ks, h, i16, (T*)nullptr), dk[t]);
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (kFast) {
+          dv[t] = mma16(pf[ks], frag16_tr_fast<G, D>(lg, ks, xt, (G*)nullptr), dv[t]);
+          dk[t] = mma16_split_a(sf[ks], frag16_tr_fast<T, D>(lq, ks, xt, (T*)nullptr), dk[t]);
+        } else {
+          const int r0 = 32 * ks + 4 * q;
+          dv[t] = mma16(pf[ks], frag16_tr<G, D>(lg, 16 * t, r0, l16, (G*)nullptr), dv[t]);
+          dk[t] = mma16_split_a(sf[ks], frag16_tr<T, D>(lq, 16 * t, r0, l16, (T*)nullptr), dk[t]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if (n > 0) request(list[e0], q0, g0, st0);
+  dma_wait();
+  __syncthreads();
+  // two tiles per trip so that every LDS buffer is a distinct object (the next
+  // tile's direct loads never alias the reads of the current one)
+  for (int e = 0; e < n; e += 2) {
+    if (e + 1 < n) request(list[e0 + e + 1], q1, g1, st1);
+    compute(q0, g0, st0);
+    dma_wait();
+    __syncthreads();
+    if (e + 1 >= n) break;
+    if (e + 2 < n) request(list[e0 + e + 2], q0, g0, st0);
+    compute(q1, g1, st1);
+    dma_wait();
+    __syncthreads();
   }
 
-  // store: lane holds d column 32t + l32, key rows 32w + 8g + 4h + i
+  // store: lane holds d column 16t + l16, key rows 16w + 4q + i
 #pragma unroll
-  for (int gq = 0; gq < 4; ++gq) {
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * q + i;
+    if (r < g.T) {
+      const size_t orow = head_off + (size_t)(jbase + member_offset(g, r)) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 32 * w + 8 * gq + 4 * h + i;
-      if (r < g.T) {
-        const size_t orow = head_off + (size_t)(jbase + member_offset(g, r)) * D;
-#pragma unroll
-        for (int t = 0; t < C::kDTiles; ++t) {
-          store1(a.dK, orow + 32 * t + l32, a.out_f32, a.scale * dk[t][4 * gq + i]);
-          store1(a.dV, orow + 32 * t + l32, a.out_f32, dv[t][4 * gq + i]);
-        }
+      for (int t = 0; t < DT; ++t) {
+        store1(a.dK, orow + 16 * t + l16, a.out_f32, a.scale * dk[t][i]);
+        store1(a.dV, orow + 16 * t + l16, a.out_f32, dv[t][i]);
       }
     }
   }
@@ -437,14 +489,19 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, int io_f32, int d, hipStream_t s
   return d == 64 ? launch_prepare_t<bf16, 64>(a, s) : launch_prepare_t<bf16, 128>(a, s);
 }
 
+template <typename T, int D>
+void launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid(a.BH * a.g.NB), block(256);
+  if (a.g.T == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, block, 0, s, a);
+}
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
-  const dim3 grid(a.BH * a.g.NB), block(kTileThreads);
   if (io_f32) {
-    if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<float, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<float, 128>), grid, block, 0, s, a);
+    if (d == 64) launch_dkdv_t<float, 64>(a, s);
+    else launch_dkdv_t<float, 128>(a, s);
   } else {
-    if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, 128>), grid, block, 0, s, a);
+    if (d == 64) launch_dkdv_t<bf16, 64>(a, s);
+    else launch_dkdv_t<bf16, 128>(a, s);
   }
   return hipGetLastError();
 }

@@ -72,6 +72,7 @@ struct BwdArgs {
   void* dV;
   // workspace views
   float* Dvec;          // [BH, N]
+  void* dO16;           // [BH, N, d] fp16 copy of dO (bf16 inputs; written by prepare)
   uint32_t* bitmap;     // [BH, NB, words]   bit tau of row j: tile tau kept block j
   int32_t* counts;      // [BH, NB]
   int32_t* offsets;     // [BH, NB + 1]

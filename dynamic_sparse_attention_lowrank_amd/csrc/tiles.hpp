@@ -108,6 +108,20 @@ __device__ __forceinline__ bf16x8 frag_tr_rows(const u32x4* lds, int col0, int s
   return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
 }
 template <typename T, int D>
+__device__ __forceinline__ f16x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, f16*) {
+  typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const int col = col0 + 4 * (i & 3);
+  const int chunk = col >> 3, byte = (col & 7) * 2;
+  const int r1 = 16 * s + 4 * h + (i >> 2), r2 = r1 + 8;
+  const char* base = reinterpret_cast<const char*>(lds);
+  const f16x4 v1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (h4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r1, chunk) * 16 + byte)));
+  const f16x4 v2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (h4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r2, chunk) * 16 + byte)));
+  return f16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+}
+template <typename T, int D>
 __device__ __forceinline__ f32x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, float*) {
   const int col = col0 + i;
   const int chunk = col >> 2, within = col & 3;
@@ -120,6 +134,178 @@ __device__ __forceinline__ f32x8 frag_tr_rows(const u32x4* lds, int col0, int s,
   }
   return r;
 }
+
+// --- 16x16x32 matrix-core helpers ---------------------------------------------
+// v_mfma_f32_16x16x32 (bf16 / fp16; fp32 as eight 16x16x4 steps over the same
+// registers).  Layout (checked on the hardware): A (16 x 32) lane l holds row l%16
+// and reduction elements 8*(l/16)..+7; B (32 x 16) lane l holds column l%16 and
+// the same elements; the 16x16 result gives lane l column l%16 and rows
+// 4*(l/16) + i in register i.
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x8 a, f32x8 b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ f32x4 mma16_split_a(const SplitBF16& a, bf16x8 b, f32x4 acc) {
+  acc = mma16(a.hi, b, acc);
+  return mma16(a.lo, b, acc);
+}
+__device__ __forceinline__ f32x4 mma16_split_a(const SplitF32& a, f32x8 b, f32x4 acc) { return mma16(a.hi, b, acc); }
+
+// row-major tile, row r, 32-wide reduction step s, lane group q = l/16 -> elements 32s+8q..+7
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag frag16_row(const u32x4* lds, int r, int s, int q) {
+  using C = TileCfg<T, D>;
+  const int c0 = (32 * s + 8 * q) / C::kCE;
+  u32x4 ch[C::kFC];
+#pragma unroll
+  for (int p = 0; p < C::kFC; ++p) ch[p] = lds[row_slot<T, D>(r, c0 + p)];
+  return frag_from_chunks(ch, (T*)nullptr);
+}
+// one token row from global memory as 16x16x32 B fragments (elements 32s+8q..+7)
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frags16(typename Elem<T>::frag* f, const T* __restrict__ row, bool ok, int q) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    u32x4 ch[C::kFC];
+#pragma unroll
+    for (int p = 0; p < C::kFC; ++p)
+      ch[p] = ok ? *reinterpret_cast<const u32x4*>(row + 32 * s + 8 * q + p * C::kCE) : u32x4{0, 0, 0, 0};
+    f[s] = frag_from_chunks(ch, (T*)nullptr);
+  }
+}
+// Transposed 16x16x32 operand from a row-major tile whose rows are the reduction
+// index: lane l gets column col0 + l%16 of rows {r0 + e : e < 4} and {r0 + 16 + e : e < 4}
+// (r0 = 32*ks + 4*(l/16) for the k-slot order of a 16x16 result taken as operand).
+template <typename T, int D>
+__device__ __forceinline__ bf16x8 frag16_tr(const u32x4* lds, int col0, int r0, int i, bf16*) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int col = col0 + 4 * (i & 3);
+  const int chunk = col >> 3, byte = (col & 7) * 2;
+  const int r1 = r0 + (i >> 2), r2 = r1 + 16;
+  const char* base = reinterpret_cast<const char*>(lds);
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r1, chunk) * 16 + byte));
+  const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r2, chunk) * 16 + byte));
+  return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+}
+template <typename T, int D>
+__device__ __forceinline__ f16x8 frag16_tr(const u32x4* lds, int col0, int r0, int i, f16*) {
+  typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const int col = col0 + 4 * (i & 3);
+  const int chunk = col >> 3, byte = (col & 7) * 2;
+  const int r1 = r0 + (i >> 2), r2 = r1 + 16;
+  const char* base = reinterpret_cast<const char*>(lds);
+  const f16x4 v1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (h4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r1, chunk) * 16 + byte)));
+  const f16x4 v2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (h4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r2, chunk) * 16 + byte)));
+  return f16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+}
+template <typename T, int D>
+__device__ __forceinline__ f32x8 frag16_tr(const u32x4* lds, int col0, int r0, int i, float*) {
+  const int col = col0 + i;
+  const int chunk = col >> 2, within = col & 3;
+  const float* base = reinterpret_cast<const float*>(lds);
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = r0 + (e < 4 ? e : 16 + e - 4);
+    r[e] = base[row_slot<T, D>(row, chunk) * 4 + within];
+  }
+  return r;
+}
+
+// Closed forms of the two 16-bit operand reads above for the XOR-swizzled layout
+// (2-byte elements, CPR = D/8 chunks per row): the lane-dependent part of the
+// byte address is one constant per lane, and the reduction step (row reads) or
+// the output tile t (transposed reads) enters by an XOR with 64*s or 32*t -- one
+// VALU op per step -- while rows and buffers are immediate offsets.
+template <int D>
+__device__ __forceinline__ int row_lane16(int l16, int q) {
+  constexpr int CPR = D / 8;
+  const int rl = l16 & (CPR - 1);
+  return l16 * CPR * 16 + 64 * (rl >> 2) + 16 * (q ^ (rl & 3));
+}
+template <int D>
+__device__ __forceinline__ int tr_lane16(int i, int q) {
+  constexpr int CPR = D / 8;
+  const int x = 4 * q + (i >> 2), rl = x & (CPR - 1), cl = (i >> 1) & 1;
+  return x * CPR * 16 + 32 * (rl >> 1) + 16 * (cl ^ (rl & 1)) + 8 * (i & 1);
+}
+// frag16_row(lds, 16*mt + l16, s, q) for 16-bit tiles; `lane_xs` = row_lane16 ^ (64*s)
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag frag16_row_fast(const u32x4* lds, int mt, int lane_xs) {
+  const char* p = reinterpret_cast<const char*>(lds) + mt * 16 * (D / 8) * 16 + lane_xs;
+  return __builtin_bit_cast(typename Elem<T>::frag, *reinterpret_cast<const u32x4*>(p));
+}
+// frag16_tr(lds, 16*t, 32*ks + 4q, l16) for 16-bit tiles; `lane_xt` = tr_lane16 ^ (32*t)
+template <typename T, int D>
+__device__ __forceinline__ bf16x8 frag16_tr_fast(const u32x4* lds, int ks, int lane_xt, bf16*) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const char* base = reinterpret_cast<const char*>(lds) + 32 * ks * (D / 8) * 16 + lane_xt;
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)base);
+  const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4 __attribute__((address_space(3)))*)(base + 16 * (D / 8) * 16));
+  return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+}
+template <typename T, int D>
+__device__ __forceinline__ f16x8 frag16_tr_fast(const u32x4* lds, int ks, int lane_xt, f16*) {
+  typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const char* base = reinterpret_cast<const char*>(lds) + 32 * ks * (D / 8) * 16 + lane_xt;
+  const f16x4 v1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((h4 __attribute__((address_space(3)))*)base));
+  const f16x4 v2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (h4 __attribute__((address_space(3)))*)(base + 16 * (D / 8) * 16)));
+  return f16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+}
+
+// --- direct global -> LDS tile loads (no register staging) --------------------
+// A row-major tile of 64 token rows, written with the XOR-swizzled slots of
+// row_slot: LDS chunk position p (row p / CPR, slot p % CPR) receives global chunk
+// slot ^ (row mod RSw) of that row.  One global_load_lds_dwordx4 moves 64 chunks
+// (1 KB); a work-group of W waves issues instructions w, w+W, ...  `off[i]` is the
+// element offset (relative to the tile's first token) that this lane loads in its
+// i-th instruction; padding rows (>= T) repeat row 0 and must be masked by the user.
+template <typename T, int D, int W>
+struct DmaCfg {
+  static constexpr int kInstr = TileCfg<T, D>::kRowChunks / 64;   // instructions per tile
+  static constexpr int kPer = kInstr / W;                          // per wave
+  static_assert(kInstr % W == 0, "tile chunks must split evenly over the waves");
+};
+template <typename T, int D, int W>
+__device__ __forceinline__ void dma_offsets(int* off, const Geo& g, int w, int lane) {
+  using C = TileCfg<T, D>;
+#pragma unroll
+  for (int i = 0; i < DmaCfg<T, D, W>::kPer; ++i) {
+    const int p = 64 * (w + W * i) + lane;
+    const int r = p / C::kCPR, s = p % C::kCPR;
+    const int c = s ^ (r & (C::kRSw - 1));
+    off[i] = (r < g.T ? member_offset(g, r) : 0) * D + c * C::kCE;
+  }
+}
+template <typename T, int D, int W>
+__device__ __forceinline__ void dma_tile(u32x4* lds, const T* __restrict__ src, const int* off, int w) {
+#pragma unroll
+  for (int i = 0; i < DmaCfg<T, D, W>::kPer; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (__attribute__((address_space(3))) void*)(lds + 64 * (w + W * i)),
+                                     16, 0, 0);
+}
+// 64 floats of one tile row each (e.g. LSE): lane l loads the value of member row l
+__device__ __forceinline__ void dma_row_stats(float* lds, const float* __restrict__ src, int off) {
+  __builtin_amdgcn_global_load_lds((const void*)(src + off), (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// wait for this wave's direct loads (vmcnt(0), other counters untouched)
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // --- staging: global -> registers -> LDS --------------------------------------
 // Row items: per thread kRowPer chunks; `off[i]` = token offset (relative to the

@@ -146,8 +146,9 @@ DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const voi
 
 /*
  * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for
- * this shape and kmax (0 on invalid arguments).  It holds D = rowsum(dO * O)
- * and the reverse (key block -> query tiles) index of idx.
+ * this shape and kmax (0 on invalid arguments).  It holds D = rowsum(dO * O),
+ * the reverse (key block -> query tiles) index of idx and, for bf16 inputs, an
+ * fp16 copy of dO (B*H*N*d*2 bytes) for the fp16 products of the backward.
  */
 DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
 
@@ -164,8 +165,10 @@ DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax
  *   dQ, dK, dV: outputs [B,H,N,d] of out_dtype, fully overwritten.
  *   workspace: device memory of at least dsa_attn_bwd_workspace_bytes(shape, kmax)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
- *   Products with the in-kernel fp32 P and dS use a bf16 hi+lo pair (two matrix-
- *   core passes), so their accuracy does not depend on the scale of dO.
+ *   Precision with bf16 inputs: dV = P^T dO runs on fp16 matrix cores (P in [0,1]
+ *   rounded to fp16, dO converted to fp16: exact for |dO| < 65504, a precondition
+ *   like the one on V in dsa_attn_fwd); products with dS use a bf16 hi+lo pair
+ *   (two matrix-core passes), so their accuracy does not depend on the scale of dS.
  *   The same device-side robustness rules as dsa_attn_fwd apply.
  */
 DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V,
