@@ -266,22 +266,52 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](const u32x4* lq, const u32x4* lg, const float (*lst)[64]) {
     // S and dP: lane holds key column kr, query rows 16mt + 4q + i
     f32x4 sacc[4], pacc[4];
+    constexpr int NS = 4 * KS;                // (mt, s) steps
+    constexpr int NT = 2 * DT;                // (t, ks) steps
+    // 16-bit path: operand reads run two steps ahead of the products (rings of 3)
+    GFrag bg[3];
+    Frag bq[3];
+    if constexpr (kFast) {
+      Frag qa[3];
+      GFrag ga[3];
+      auto rd = [&](int k, Frag& qf, GFrag& gf) {
+        const int xs = rowl ^ (64 * (k % KS));
+        qf = frag16_row_fast<T, D>(lq, k / KS, xs);
+        gf = frag16_row_fast<G, D>(lg, k / KS, xs);
+      };
+      auto rt = [&](int k, GFrag& gb, Frag& qb) {
+        const int xt = trl ^ (32 * (k / 2));
+        gb = frag16_tr_fast<G, D>(lg, k % 2, xt, (G*)nullptr);
+        qb = frag16_tr_fast<T, D>(lq, k % 2, xt, (T*)nullptr);
+      };
+      rd(0, qa[0], ga[0]);
+      rd(1, qa[1], ga[1]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = f32x4{};
-      pacc[mt] = f32x4{};
+      for (int k = 0; k < NS; ++k) {
+        if (k + 2 < NS) rd(k + 2, qa[(k + 2) % 3], ga[(k + 2) % 3]);
+        const int mt = k / KS, s = k % KS;
+        if (s == 0) {
+          sacc[mt] = f32x4{};
+          pacc[mt] = f32x4{};
+        }
+        sacc[mt] = mma16(qa[k % 3], kf[s], sacc[mt]);
+        pacc[mt] = mma16(ga[k % 3], vf[s], pacc[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rt(0, bg[0], bq[0]);                    // first transposed operands, under the softmax below
+      rt(1, bg[1], bq[1]);
+    } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (kFast) {
-          const int xs = rowl ^ (64 * s);
-          sacc[mt] = mma16(frag16_row_fast<T, D>(lq, mt, xs), kf[s], sacc[mt]);
-          pacc[mt] = mma16(frag16_row_fast<G, D>(lg, mt, xs), vf[s], pacc[mt]);
-        } else {
+      for (int mt = 0; mt < 4; ++mt) {
+        sacc[mt] = f32x4{};
+        pacc[mt] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
           sacc[mt] = mma16(frag16_row<T, D>(lq, 16 * mt + l16, s, q), kf[s], sacc[mt]);
           pacc[mt] = mma16(frag16_row<G, D>(lg, 16 * mt + l16, s, q), vf[s], pacc[mt]);
         }
+        __builtin_amdgcn_sched_barrier(0);      // bounds the operand reads in flight
       }
-      __builtin_amdgcn_sched_barrier(0);      // bounds the operand reads in flight
     }
     // P and dS as A operands: k-slot e of step ks <-> query 32ks + 16(e/4) + 4q + e%4
     GFrag pf[2];
@@ -305,22 +335,33 @@ void bwd_dkdv_kernel(BwdArgs a) {
       pf[ks] = to_frag(pv, (G*)nullptr);
       to_split(sv, sf[ks]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // dV += P^T dO, dK += dS^T Q: lane holds d column 16t + l16, key rows 4q + i
+    if constexpr (kFast) {
+      auto rt = [&](int k, GFrag& gb, Frag& qb) {
+        const int xt = trl ^ (32 * (k / 2));
+        gb = frag16_tr_fast<G, D>(lg, k % 2, xt, (G*)nullptr);
+        qb = frag16_tr_fast<T, D>(lq, k % 2, xt, (T*)nullptr);
+      };
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const int xt = trl ^ (32 * t);
+      for (int k = 0; k < NT; ++k) {
+        if (k + 2 < NT) rt(k + 2, bg[(k + 2) % 3], bq[(k + 2) % 3]);
+        const int t = k / 2, ks = k % 2;
+        dv[t] = mma16(pf[ks], bg[k % 3], dv[t]);
+        dk[t] = mma16_split_a(sf[ks], bq[k % 3], dk[t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if constexpr (kFast) {
-          dv[t] = mma16(pf[ks], frag16_tr_fast<G, D>(lg, ks, xt, (G*)nullptr), dv[t]);
-          dk[t] = mma16_split_a(sf[ks], frag16_tr_fast<T, D>(lq, ks, xt, (T*)nullptr), dk[t]);
-        } else {
+      for (int t = 0; t < DT; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
           const int r0 = 32 * ks + 4 * q;
           dv[t] = mma16(pf[ks], frag16_tr<G, D>(lg, 16 * t, r0, l16, (G*)nullptr), dv[t]);
           dk[t] = mma16_split_a(sf[ks], frag16_tr<T, D>(lq, 16 * t, r0, l16, (T*)nullptr), dk[t]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

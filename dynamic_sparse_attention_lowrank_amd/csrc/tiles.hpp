@@ -1,11 +1,11 @@
 // LDS staging of 64-token tiles for the attention kernels (gfx950).
 //
-// A work-group has 2 waves (128 threads); each wave owns 32 rows of a 64-row
-// operand tile.  Two LDS layouts are used for a tile of 64 tokens x D elements:
+// Tiles of 64 tokens x D elements.  Two LDS layouts are used:
 //
 //  * row-major  [64][D]: a token row is D*sizeof(T) bytes = CPR 16-byte chunks;
-//    chunk c of row r sits at slot c ^ (r mod min(CPR,16)), so the 32 lanes that
-//    read one chunk column of 32 consecutive rows hit distinct banks;
+//    chunk c of row r sits at slot c ^ row_swz(r) (a bijection of r mod
+//    min(CPR,16)), so both the row-wise operand reads and the transposing reads
+//    of 4-row groups are free of bank conflicts;
 //  * transposed [D][64]: row d holds element d of all 64 tokens, with token
 //    position p = 16*G + perm16(k) for token 16*G + k (see common.hpp), so that
 //    one 16-byte read gives a lane the 8 tokens its MFMA operand needs.  Chunk c
@@ -41,10 +41,18 @@ struct TileCfg {
   static constexpr int kTrChunks = D * kTR;                   // LDS chunks of a transposed tile
 };
 
+// Row swizzle: a bijection of r mod RSw whose bits 1-2 are r mod 4 (bit 0: bit 2 of
+// r, bit 3: bit 3 of r).  16 consecutive rows reading one chunk column hit 16
+// distinct slots, and 4 consecutive rows (starting at a multiple of 4) reading a
+// 32-byte column pair hit 8 distinct slots -- both conflict-free at d = 128.
+template <typename T, int D>
+__device__ __forceinline__ int row_swz(int r) {
+  return (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8)) & (TileCfg<T, D>::kRSw - 1);
+}
 template <typename T, int D>
 __device__ __forceinline__ int row_slot(int r, int c) {
   using C = TileCfg<T, D>;
-  return r * C::kCPR + (c ^ (r & (C::kRSw - 1)));
+  return r * C::kCPR + (c ^ row_swz<T, D>(r));
 }
 template <typename T, int D>
 __device__ __forceinline__ int tr_slot(int d, int c) {
@@ -233,14 +241,14 @@ __device__ __forceinline__ f32x8 frag16_tr(const u32x4* lds, int col0, int r0, i
 template <int D>
 __device__ __forceinline__ int row_lane16(int l16, int q) {
   constexpr int CPR = D / 8;
-  const int rl = l16 & (CPR - 1);
-  return l16 * CPR * 16 + 64 * (rl >> 2) + 16 * (q ^ (rl & 3));
+  const int f = row_swz<bf16, D>(l16);
+  return l16 * CPR * 16 + 64 * (f >> 2) + 16 * (q ^ (f & 3));
 }
 template <int D>
 __device__ __forceinline__ int tr_lane16(int i, int q) {
   constexpr int CPR = D / 8;
-  const int x = 4 * q + (i >> 2), rl = x & (CPR - 1), cl = (i >> 1) & 1;
-  return x * CPR * 16 + 32 * (rl >> 1) + 16 * (cl ^ (rl & 1)) + 8 * (i & 1);
+  const int x = 4 * q + (i >> 2), f = row_swz<bf16, D>(x), cl = (i >> 1) & 1;
+  return x * CPR * 16 + 32 * (f >> 1) + 16 * (cl ^ (f & 1)) + 8 * (i & 1);
 }
 // frag16_row(lds, 16*mt + l16, s, q) for 16-bit tiles; `lane_xs` = row_lane16 ^ (64*s)
 template <typename T, int D>
@@ -289,7 +297,7 @@ __device__ __forceinline__ void dma_offsets(int* off, const Geo& g, int w, int l
   for (int i = 0; i < DmaCfg<T, D, W>::kPer; ++i) {
     const int p = 64 * (w + W * i) + lane;
     const int r = p / C::kCPR, s = p % C::kCPR;
-    const int c = s ^ (r & (C::kRSw - 1));
+    const int c = s ^ row_swz<T, D>(r);
     off[i] = (r < g.T ? member_offset(g, r) : 0) * D + c * C::kCE;
   }
 }
