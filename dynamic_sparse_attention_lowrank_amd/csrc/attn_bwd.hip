@@ -257,20 +257,23 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool kFast = sizeof(T) == 2;
   const int rowl = row_lane16<D>(l16, q), trl = tr_lane16<D>(l16, q);
 
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Qh, (size_t)g.N * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rg = head_rsrc(Gh, (size_t)g.N * D * sizeof(G));
+  const __amdgpu_buffer_rsrc_t rs = head_rsrc(w == 0 ? LSEh : Dh, (size_t)g.N * sizeof(float));
   auto request = [&](int tau, u32x4* lq, u32x4* lg, float (*lst)[64]) {
     const int base = tile_base(g, tau);
-    dma_tile<T, D, W>(lq, Qh + (size_t)base * D, qoff, w);
-    dma_tile<G, D, W>(lg, Gh + (size_t)base * D, goff, w);
-    if (w < 2) dma_row_stats(lst[w], (w == 0 ? LSEh : Dh) + base, soff);
+    dma_tile<T, D, W>(lq, rq, base * D * (int)sizeof(T), qoff, w);
+    dma_tile<G, D, W>(lg, rg, base * D * (int)sizeof(G), goff, w);
+    if (w < 2) dma_row_stats(lst[w], rs, base * 4, soff);
   };
   auto compute = [&](const u32x4* lq, const u32x4* lg, const float (*lst)[64]) {
     // S and dP: lane holds key column kr, query rows 16mt + 4q + i
     f32x4 sacc[4], pacc[4];
     constexpr int NS = 4 * KS;                // (mt, s) steps
     constexpr int NT = 2 * DT;                // (t, ks) steps
-    // 16-bit path: operand reads run two steps ahead of the products (rings of 3)
-    GFrag bg[3];
-    Frag bq[3];
+    // 16-bit path: operand reads run two steps ahead of the products
+    GFrag bg[4];
+    Frag bq[4];
     if constexpr (kFast) {
       Frag qa[3];
       GFrag ga[3];
@@ -279,10 +282,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
         qf = frag16_row_fast<T, D>(lq, k / KS, xs);
         gf = frag16_row_fast<G, D>(lg, k / KS, xs);
       };
-      auto rt = [&](int k, GFrag& gb, Frag& qb) {
-        const int xt = trl ^ (32 * (k / 2));
-        gb = frag16_tr_fast<G, D>(lg, k % 2, xt, (G*)nullptr);
-        qb = frag16_tr_fast<T, D>(lq, k % 2, xt, (T*)nullptr);
+      auto rt = [&](int k, GFrag& gb, Frag& qb) {   // step k = (t, ks) as in the dV/dK loop below
+        const int t = 2 * (k / 4) + (k & 1), ks = (k >> 1) & 1;
+        const int xt = trl ^ (32 * t);
+        gb = frag16_tr_fast<G, D>(lg, ks, xt, (G*)nullptr);
+        qb = frag16_tr_fast<T, D>(lq, ks, xt, (T*)nullptr);
       };
       rd(0, qa[0], ga[0]);
       rd(1, qa[1], ga[1]);
@@ -338,17 +342,28 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // dV += P^T dO, dK += dS^T Q: lane holds d column 16t + l16, key rows 4q + i
     if constexpr (kFast) {
+      // steps k = (t, ks) in the order (t0, ks), (t0+1, ks) so that the hi and lo
+      // passes of dK never depend on the product issued just before them
       auto rt = [&](int k, GFrag& gb, Frag& qb) {
-        const int xt = trl ^ (32 * (k / 2));
-        gb = frag16_tr_fast<G, D>(lg, k % 2, xt, (G*)nullptr);
-        qb = frag16_tr_fast<T, D>(lq, k % 2, xt, (T*)nullptr);
+        const int t = 2 * (k / 4) + (k & 1), ks = (k >> 1) & 1;
+        const int xt = trl ^ (32 * t);
+        gb = frag16_tr_fast<G, D>(lg, ks, xt, (G*)nullptr);
+        qb = frag16_tr_fast<T, D>(lq, ks, xt, (T*)nullptr);
       };
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        if (k + 2 < NT) rt(k + 2, bg[(k + 2) % 3], bq[(k + 2) % 3]);
-        const int t = k / 2, ks = k % 2;
-        dv[t] = mma16(pf[ks], bg[k % 3], dv[t]);
-        dk[t] = mma16_split_a(sf[ks], bq[k % 3], dk[t]);
+      for (int k = 0; k < NT; k += 2) {
+        if (k + 2 < NT) rt(k + 2, bg[(k + 2) % 4], bq[(k + 2) % 4]);
+        if (k + 3 < NT) rt(k + 3, bg[(k + 3) % 4], bq[(k + 3) % 4]);
+        const int t0 = 2 * (k / 4), ks = (k >> 1) & 1;
+        const int a0 = k % 4, a1 = (k + 1) % 4;
+        dv[t0] = mma16(pf[ks], bg[a0], dv[t0]);
+        dv[t0 + 1] = mma16(pf[ks], bg[a1], dv[t0 + 1]);
+        if constexpr (__is_same(T, bf16)) {
+          dk[t0] = mma16(sf[ks].hi, bq[a0], dk[t0]);
+          dk[t0 + 1] = mma16(sf[ks].hi, bq[a1], dk[t0 + 1]);
+          dk[t0] = mma16(sf[ks].lo, bq[a0], dk[t0]);
+          dk[t0 + 1] = mma16(sf[ks].lo, bq[a1], dk[t0 + 1]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {

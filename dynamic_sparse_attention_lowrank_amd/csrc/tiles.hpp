@@ -301,16 +301,22 @@ __device__ __forceinline__ void dma_offsets(int* off, const Geo& g, int w, int l
     off[i] = (r < g.T ? member_offset(g, r) : 0) * D + c * C::kCE;
   }
 }
+// Buffer-resource form (MUBUF "buffer_load ... lds"): unlike the global form it
+// leaves the compiler's LDS-read wait counts exact.  `rsrc` covers one head;
+// `tile_bytes` is the byte offset of the tile's first token row.
 template <typename T, int D, int W>
-__device__ __forceinline__ void dma_tile(u32x4* lds, const T* __restrict__ src, const int* off, int w) {
+__device__ __forceinline__ void dma_tile(u32x4* lds, __amdgpu_buffer_rsrc_t rsrc, int tile_bytes, const int* off, int w) {
 #pragma unroll
   for (int i = 0; i < DmaCfg<T, D, W>::kPer; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (__attribute__((address_space(3))) void*)(lds + 64 * (w + W * i)),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + 64 * (w + W * i)), 16,
+                                             off[i] * (int)sizeof(T), tile_bytes, 0, 0);
 }
 // 64 floats of one tile row each (e.g. LSE): lane l loads the value of member row l
-__device__ __forceinline__ void dma_row_stats(float* lds, const float* __restrict__ src, int off) {
-  __builtin_amdgcn_global_load_lds((const void*)(src + off), (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+__device__ __forceinline__ void dma_row_stats(float* lds, __amdgpu_buffer_rsrc_t rsrc, int tile_bytes, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, off * 4, tile_bytes, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
 // wait for this wave's direct loads (vmcnt(0), other counters untouched)
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
