@@ -6,23 +6,27 @@
 //   D_i = dO_i . O_i,  dS_in = P_in (dO_i . v_n - D_i),
 //   dQ_i = scale sum_n dS_in k_n,  dK_n = scale sum_i dS_in q_i,  dV_n = sum_i P_in dO_i.
 //
-// Precision: the probabilities P and dS are computed in fp32 inside the
-// kernels; where they feed a matrix-core product with bf16 inputs they are
-// carried as a bf16 pair (hi + lo, see common.hpp) and the product is issued
-// twice, so the gradients keep fp32-level accuracy whatever the scale of dO.
-// D is taken from O as passed in (fp32 O keeps D accurate; with bf16 O its
-// rounding enters D coherently across a whole row).
+// Precision: P and dS are computed in fp32 inside the kernels.  dV = P^T dO runs
+// on fp16 matrix cores (P in [0,1] rounded to fp16, dO from an fp16 copy written
+// by the prepare phase -- exact for |dO| < 65504); the products with dS (dK, dQ)
+// take it as a bf16 pair hi + lo (see common.hpp) issued twice, so they keep
+// fp32-level accuracy whatever the scale of dS.  D is taken from O as passed in
+// (fp32 O keeps D accurate; with bf16 O its rounding enters D coherently across a
+// whole row).
 //
 // No floating-point atomics, so results are bit-reproducible:
 //   1. prep:     D (fp32) for every token;
 //   2. reverse index of the block mask: a bitmap row per key block (bit tau set
 //      if tile tau kept it; integer OR is order-free), popcounts, a per-head
 //      exclusive scan, and an ascending compaction into CSC lists;
-//   3. dK/dV:    one work-group per key block walks the query tiles that kept it
-//                (S = Q K^T and dP = dO V^T with K, V in registers; then
-//                dV += P^T dO and dK += dS^T Q from transposed Q/dO tiles in LDS);
-//   4. dQ:       one work-group per query tile walks its kept blocks like the
-//                forward (S^T = K Q^T, dP^T = V dO^T; dQ^T += K^T dS^T).
+//   3. dK/dV:    one work-group (4 waves, 16 keys each) per key block walks the
+//                query tiles that kept it (S = Q K^T and dP = dO V^T with K, V in
+//                registers; dV += P^T dO and dK += dS^T Q with Q / dO read
+//                transposed from LDS);
+//   4. dQ:       one work-group (4 waves, 16 queries each) per query tile walks
+//                its kept blocks (S^T = K Q^T, dP^T = V dO^T; dQ^T += K^T dS^T).
+// Both stream their tiles through double-buffered LDS filled by direct
+// global->LDS loads, one tile ahead of the computation.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -413,20 +417,35 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 4. dQ
-template <typename T, int D>
-__global__ __launch_bounds__(kTileThreads) void bwd_dq_kernel(BwdArgs a) {
+// One work-group of 4 waves per query tile, two waves per SIMD; wave w owns
+// queries 16w..16w+15, whose Q and dO rows stay in registers as the B operands of
+// the 16x16x32 products S^T = K Q^T and dP^T = V dO^T (all bf16).  The kept
+// blocks stream through two LDS buffers (K and V rows), filled by direct
+// global->LDS loads one block ahead.  Per block and wave:
+//   S^T, dP^T (64 keys x 16 queries)   A = K / V rows (ds_read_b128), 4 x 4 MFMA each
+//   P^T = exp2(S^T c - LSE log2 e), dS^T = P^T (dP^T - D)   lane = query column
+//   dQ^T += K^T dS^T                   B = dS^T straight from the S^T registers (bf16
+//                                      hi+lo), A = K read transposed (ds_read_b64_tr_b16)
+template <typename T, int D, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
+  constexpr int W = 4;
   using C = TileCfg<T, D>;
   typedef typename Elem<T>::frag Frag;
-  __shared__ u32x4 lds_k[C::kRowChunks];
-  __shared__ u32x4 lds_kt[C::kTrChunks];
-  __shared__ u32x4 lds_v[C::kRowChunks];
+  typedef typename SplitOf<T>::type Split;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr bool kFast = sizeof(T) == 2;
+  __shared__ u32x4 k0[C::kRowChunks], k1[C::kRowChunks];
+  __shared__ u32x4 v0[C::kRowChunks], v1[C::kRowChunks];
 
   const Geo g = a.g;
   const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
   const int bh = L / g.NB;
   const int tau = L - bh * g.NB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
   const size_t head_off = (size_t)bh * g.N * D;
   const T* __restrict__ Kh = reinterpret_cast<const T*>(a.K) + head_off;
   const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + head_off;
@@ -434,89 +453,172 @@ __global__ __launch_bounds__(kTileThreads) void bwd_dq_kernel(BwdArgs a) {
   int kk = a.kvec[bh];
   kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
 
-  const int q = 32 * wave + l32;
-  const bool q_ok = q < g.T;
-  const int q_tok = tile_base(g, tau) + (q_ok ? member_offset(g, q) : 0);
-  Frag qf[C::kSteps], gf[C::kSteps];
-  load_row_frags<T, D>(qf, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, h);
-  load_row_frags<T, D>(gf, reinterpret_cast<const T*>(a.dO) + head_off + (size_t)q_tok * D, q_ok, h);
-  const float lse2 = q_ok ? a.LSE[(size_t)bh * g.N + q_tok] * kLog2e : INFINITY;
-  const float dv = q_ok ? a.Dvec[(size_t)bh * g.N + q_tok] : 0.f;
+  // this lane's query row (B fragments: N = queries)
+  const int qr = 16 * w + l16;
+  const bool q_ok = qr < g.T;
+  const int q_tok = tile_base(g, tau) + (q_ok ? member_offset(g, qr) : 0);
+  Frag qf[KS], gf[KS];
+  load_row_frags16<T, D>(qf, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, q);
+  load_row_frags16<T, D>(gf, reinterpret_cast<const T*>(a.dO) + head_off + (size_t)q_tok * D, q_ok, q);
+  const float nl = q_ok ? -a.LSE[(size_t)bh * g.N + q_tok] * kLog2e : -INFINITY;   // padding rows: P = 0
+  const float dd = q_ok ? a.Dvec[(size_t)bh * g.N + q_tok] : 0.f;
 
-  int koff[C::kGPer][8];
-  group_offsets<T, D>(koff, g, tid);
-  int voff[C::kRowPer];
-  row_offsets<T, D>(voff, g, tid);
+  int koff[DmaCfg<T, D, W>::kPer];
+  dma_offsets<T, D, W>(koff, g, w, lane);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(Kh, (size_t)g.N * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(Vh, (size_t)g.N * D * sizeof(T));
+  const int rowl = kFast ? row_lane16<D>(l16, q) : 0, trl = kFast ? tr_lane16<D>(l16, q) : 0;
 
-  f32x16 dqacc[C::kDTiles];
+  f32x4 dq[DT];
 #pragma unroll
-  for (int t = 0; t < C::kDTiles; ++t) dqacc[t] = f32x16{};
+  for (int t = 0; t < DT; ++t) dq[t] = f32x4{};
   const float c2 = a.c;
 
-  int slot = 0;
-  while (slot < kk && (unsigned)irow[slot] >= (unsigned)g.NB) ++slot;
-  GroupStage<T, D> kst;
-  RowStage<T, D> vst;
-  if (slot < kk) {
-    const int base = tile_base(g, irow[slot]);
-    group_load<T, D>(kst, Kh, base, koff, tid);
-    row_load<T, D>(vst, Vh, base, voff, tid);
-  }
-  while (slot < kk) {
-    __syncthreads();
-    group_store<T, D>(kst, lds_kt, lds_k, tid);
-    row_store<T, D>(vst, lds_v, tid);
-    __syncthreads();
-    int nxt = slot + 1;
-    while (nxt < kk && (unsigned)irow[nxt] >= (unsigned)g.NB) ++nxt;
-    if (nxt < kk) {
-      const int base = tile_base(g, irow[nxt]);
-      group_load<T, D>(kst, Kh, base, koff, tid);
-      row_load<T, D>(vst, Vh, base, voff, tid);
-    }
-
-    f32x16 sacc[2], pacc[2];
+  auto request = [&](int blk, u32x4* lk, u32x4* lv) {
+    const int base = tile_base(g, blk);
+    dma_tile<T, D, W>(lk, rk, base * D * (int)sizeof(T), koff, w);
+    dma_tile<T, D, W>(lv, rv, base * D * (int)sizeof(T), koff, w);
+  };
+  auto compute = [&](const u32x4* lk, const u32x4* lv) {
+    // S^T and dP^T: lane holds query column qr, key rows 16mt + 4q + i
+    f32x4 sacc[4], pacc[4];
+    Frag ka[4];                                // transposed K operands of the first steps (prefetched)
+    if constexpr (kFast) {
+      Frag ra[3], rb[3];
+      auto rd = [&](int k, Frag& x, Frag& y) {
+        const int xs = rowl ^ (64 * (k % KS));
+        x = frag16_row_fast<T, D>(lk, k / KS, xs);
+        y = frag16_row_fast<T, D>(lv, k / KS, xs);
+      };
+      rd(0, ra[0], rb[0]);
+      rd(1, ra[1], rb[1]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x16{};
-      pacc[mt] = f32x16{};
+      for (int k = 0; k < 4 * KS; ++k) {
+        if (k + 2 < 4 * KS) rd(k + 2, ra[(k + 2) % 3], rb[(k + 2) % 3]);
+        const int mt = k / KS, s = k % KS;
+        if (s == 0) {
+          sacc[mt] = f32x4{};
+          pacc[mt] = f32x4{};
+        }
+        sacc[mt] = mma16(ra[k % 3], qf[s], sacc[mt]);
+        pacc[mt] = mma16(rb[k % 3], gf[s], pacc[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        sacc[mt] = mma_step(frag_row<T, D>(lds_k, 32 * mt + l32, s, h), qf[s], sacc[mt]);
-        pacc[mt] = mma_step(frag_row<T, D>(lds_v, 32 * mt + l32, s, h), gf[s], pacc[mt]);
+      for (int k = 0; k < 2; ++k) {
+        ka[2 * k] = frag16_tr_fast<T, D>(lk, 0, trl ^ (32 * k), (T*)nullptr);
+        ka[2 * k + 1] = frag16_tr_fast<T, D>(lk, 1, trl ^ (32 * k), (T*)nullptr);
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        sacc[mt] = f32x4{};
+        pacc[mt] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          sacc[mt] = mma16(frag16_row<T, D>(lk, 16 * mt + l16, s, q), qf[s], sacc[mt]);
+          pacc[mt] = mma16(frag16_row<T, D>(lv, 16 * mt + l16, s, q), gf[s], pacc[mt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    typename SplitOf<T>::type sf[4];
+    // dS^T as B operands: k-slot e of step ks <-> key 32ks + 16(e/4) + 4q + e%4
+    Split sf[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int ks = 0; ks < 2; ++ks) {
       float sv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 8 * (s & 1) + e;
-        const int key = 32 * (s >> 1) + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float p = key < g.T ? fast_exp2(fmaf(sacc[s >> 1][i], c2, -lse2)) : 0.f;
-        sv[e] = p * (pacc[s >> 1][i] - dv);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int mt = 2 * ks + hf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = fast_exp2(fmaf(sacc[mt][i], c2, nl));
+          if constexpr (!FULL) p = (16 * mt + 4 * q + i < g.T) ? p : 0.f;     // padding keys
+          sv[4 * hf + i] = p * (pacc[mt][i] - dd);
+        }
       }
-      to_split(sv, sf[s]);
+      to_split(sv, sf[ks]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // dQ^T += K^T dS^T: lane holds query column qr, d rows 16t + 4q + i
+    if constexpr (kFast) {
+      Frag kb[4];
 #pragma unroll
-    for (int t = 0; t < C::kDTiles; ++t) {
+      for (int t = 0; t < DT; t += 2) {
+        const bool pre = t + 2 < DT;
+        if (pre) {
+          kb[0] = frag16_tr_fast<T, D>(lk, 0, trl ^ (32 * (t + 2)), (T*)nullptr);
+          kb[1] = frag16_tr_fast<T, D>(lk, 1, trl ^ (32 * (t + 2)), (T*)nullptr);
+          kb[2] = frag16_tr_fast<T, D>(lk, 0, trl ^ (32 * (t + 3)), (T*)nullptr);
+          kb[3] = frag16_tr_fast<T, D>(lk, 1, trl ^ (32 * (t + 3)), (T*)nullptr);
+        }
+        // t: ka[0] (ks 0), ka[1] (ks 1); t+1: ka[2], ka[3]
+        dq[t] = mma16(ka[0], sf[0].hi, dq[t]);
+        dq[t + 1] = mma16(ka[2], sf[0].hi, dq[t + 1]);
+        dq[t] = mma16(ka[0], sf[0].lo, dq[t]);
+        dq[t + 1] = mma16(ka[2], sf[0].lo, dq[t + 1]);
+        dq[t] = mma16(ka[1], sf[1].hi, dq[t]);
+        dq[t + 1] = mma16(ka[3], sf[1].hi, dq[t + 1]);
+        dq[t] = mma16(ka[1], sf[1].lo, dq[t]);
+        dq[t + 1] = mma16(ka[3], sf[1].lo, dq[t + 1]);
+        if (pre) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dqacc[t] = mma_split_b(frag_tr<T, D>(lds_kt, 32 * t + l32, s, h), sf[s], dqacc[t]);
+          for (int x = 0; x < 4; ++x) ka[x] = kb[x];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const Frag kt = frag16_tr<T, D>(lk, 16 * t, 32 * ks + 4 * q, l16, (T*)nullptr);
+          dq[t] = mma16(kt, sf[ks].hi, dq[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    slot = nxt;
+  };
+
+  // the kept blocks in idx order, invalid entries skipped (wave-uniform)
+  int slot = 0;
+  auto next_valid = [&]() -> int {
+    while (slot < kk) {
+      const int b = irow[slot++];
+      if ((unsigned)b < (unsigned)g.NB) return b;
+    }
+    return -1;
+  };
+  int bcur = next_valid();
+  if (bcur >= 0) request(bcur, k0, v0);
+  dma_wait();
+  __syncthreads();
+  int bnext = bcur >= 0 ? next_valid() : -1;
+  // two blocks per trip so that every LDS buffer is a distinct object
+  while (bcur >= 0) {
+    if (bnext >= 0) request(bnext, k1, v1);
+    compute(k0, v0);
+    dma_wait();
+    __syncthreads();
+    bcur = bnext;
+    if (bcur < 0) break;
+    bnext = next_valid();
+    if (bnext >= 0) request(bnext, k0, v0);
+    compute(k1, v1);
+    dma_wait();
+    __syncthreads();
+    bcur = bnext;
+    if (bcur < 0) break;
+    bnext = next_valid();
   }
+
+  // store: lane holds query column qr, d rows 16t + 4q + i
   if (q_ok) {
     const size_t orow = head_off + (size_t)q_tok * D;
     const float sc = a.scale;
 #pragma unroll
-    for (int t = 0; t < C::kDTiles; ++t) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        store4(a.dQ, orow + 32 * t + 8 * gq + 4 * h, a.out_f32, sc * dqacc[t][4 * gq], sc * dqacc[t][4 * gq + 1],
-               sc * dqacc[t][4 * gq + 2], sc * dqacc[t][4 * gq + 3]);
-      }
-    }
+    for (int t = 0; t < DT; ++t)
+      store4(a.dQ, orow + 16 * t + 4 * q, a.out_f32, sc * dq[t][0], sc * dq[t][1], sc * dq[t][2], sc * dq[t][3]);
   }
 }
 
@@ -562,14 +664,19 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D>
+void launch_dq_t(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid(a.BH * a.g.NB), block(256);
+  if (a.g.T == 64) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), grid, block, 0, s, a);
+}
 hipError_t launch_bwd_dq(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
-  const dim3 grid(a.BH * a.g.NB), block(kTileThreads);
   if (io_f32) {
-    if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<float, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<float, 128>), grid, block, 0, s, a);
+    if (d == 64) launch_dq_t<float, 64>(a, s);
+    else launch_dq_t<float, 128>(a, s);
   } else {
-    if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<bf16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<bf16, 128>), grid, block, 0, s, a);
+    if (d == 64) launch_dq_t<bf16, 64>(a, s);
+    else launch_dq_t<bf16, 128>(a, s);
   }
   return hipGetLastError();
 }

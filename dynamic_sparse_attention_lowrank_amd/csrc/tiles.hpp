@@ -1,21 +1,13 @@
-// LDS staging of 64-token tiles for the attention kernels (gfx950).
+// LDS tiles of 64 tokens x D elements for the attention kernels (gfx950).
 //
-// Tiles of 64 tokens x D elements.  Two LDS layouts are used:
+// Layout: row-major [64][D]; a token row is D*sizeof(T) bytes = CPR 16-byte
+// chunks, and chunk c of row r sits at slot c ^ row_swz(r) (a bijection of
+// r mod min(CPR,16)), so both the row-wise operand reads and the transposing
+// reads of 4-row groups are free of bank conflicts at d = 128.
 //
-//  * row-major  [64][D]: a token row is D*sizeof(T) bytes = CPR 16-byte chunks;
-//    chunk c of row r sits at slot c ^ row_swz(r) (a bijection of r mod
-//    min(CPR,16)), so both the row-wise operand reads and the transposing reads
-//    of 4-row groups are free of bank conflicts;
-//  * transposed [D][64]: row d holds element d of all 64 tokens, with token
-//    position p = 16*G + perm16(k) for token 16*G + k (see common.hpp), so that
-//    one 16-byte read gives a lane the 8 tokens its MFMA operand needs.  Chunk c
-//    of row d sits at c ^ ((d ^ (d >> log2 TR)) mod TR), which keeps both the
-//    transposing writes and the operand reads spread over the banks.
-//
-// Global loads are 16-byte chunks.  A "row item" is one chunk of one token row
-// (consecutive threads take consecutive chunks of a row).  A "group item" is one
-// chunk column of the 8 tokens in one 8-position group of the transposed layout;
-// it is written both transposed and, when needed, row-major.
+// Tiles are filled either by direct global->LDS loads (dma_*: the backward) or
+// through registers (row_*: the forward's Q tile, 128 threads).  Global accesses
+// are 16-byte chunks.
 #pragma once
 
 #include "common.hpp"
@@ -30,15 +22,10 @@ struct TileCfg {
   static constexpr int kFC = Elem<T>::kFragChunks;            // chunks per MFMA fragment
   static constexpr int kCPR = D / kCE;                        // chunks per token row
   static constexpr int kRowPer = 64 * kCPR / kTileThreads;    // row items per thread
-  static constexpr int kGItems = 8 * kCPR;                    // group items per tile
-  static constexpr int kGPer = (kGItems + kTileThreads - 1) / kTileThreads;
-  static constexpr int kTR = 64 * (int)sizeof(T) / 16;        // chunks per transposed row
-  static constexpr int kTLog = kTR == 8 ? 3 : 4;
   static constexpr int kRSw = kCPR < 16 ? kCPR : 16;
   static constexpr int kSteps = D / 16;                       // reduction steps over d
   static constexpr int kDTiles = D / 32;                      // 32-wide tiles over d
   static constexpr int kRowChunks = 64 * kCPR;                // LDS chunks of a row-major tile
-  static constexpr int kTrChunks = D * kTR;                   // LDS chunks of a transposed tile
 };
 
 // Row swizzle: a bijection of r mod RSw whose bits 1-2 are r mod 4 (bit 0: bit 2 of
@@ -54,14 +41,6 @@ __device__ __forceinline__ int row_slot(int r, int c) {
   using C = TileCfg<T, D>;
   return r * C::kCPR + (c ^ row_swz<T, D>(r));
 }
-template <typename T, int D>
-__device__ __forceinline__ int tr_slot(int d, int c) {
-  using C = TileCfg<T, D>;
-  return d * C::kTR + (c ^ ((d ^ (d >> C::kTLog)) & (C::kTR - 1)));
-}
-// token position (0..63) stored at place e of 8-position group kg
-__device__ __forceinline__ int group_row(int kg, int e) { return 16 * (kg >> 1) + perm16(8 * (kg & 1) + e); }
-
 // --- A/B operand fragments from LDS -----------------------------------------
 // row-major tile: row r, reduction step s, lane half h -> elements 16s+8h..+7
 template <typename T, int D>
@@ -72,77 +51,6 @@ __device__ __forceinline__ typename Elem<T>::frag frag_row(const u32x4* lds, int
   for (int p = 0; p < C::kFC; ++p) ch[p] = lds[row_slot<T, D>(r, (2 * s + h) * C::kFC + p)];
   return frag_from_chunks(ch, (T*)nullptr);
 }
-// transposed tile: row d, token step s (16 tokens), lane half h -> positions 16s+8h..+7
-template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::frag frag_tr(const u32x4* lds, int d, int s, int h) {
-  using C = TileCfg<T, D>;
-  u32x4 ch[C::kFC];
-#pragma unroll
-  for (int p = 0; p < C::kFC; ++p) ch[p] = lds[tr_slot<T, D>(d, (2 * s + h) * C::kFC + p)];
-  return frag_from_chunks(ch, (T*)nullptr);
-}
-// one token row straight from global memory as B operand fragments (row tok, elements 16s+8h..)
-template <typename T, int D>
-__device__ __forceinline__ void load_row_frags(typename Elem<T>::frag* f, const T* __restrict__ row, bool ok, int h) {
-  using C = TileCfg<T, D>;
-#pragma unroll
-  for (int s = 0; s < C::kSteps; ++s) {
-    u32x4 ch[C::kFC];
-#pragma unroll
-    for (int p = 0; p < C::kFC; ++p)
-      ch[p] = ok ? *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * h + p * C::kCE) : u32x4{0, 0, 0, 0};
-    f[s] = frag_from_chunks(ch, (T*)nullptr);
-  }
-}
-
-// Transposed operand fragment from a row-major tile whose rows are the reduction
-// index (e.g. queries): lane l gets column col0 + l%16 (col0 = 32t + 16*((l%32)/16))
-// and the 8 rows {16s+4h+0..3, 16s+8+4h+0..3} -- the perm16 order in which the
-// P^T / dS^T fragments taken from a 32x32 result hold their reduction index.
-// 16-bit types use gfx950's transposing LDS read (ds_read_b64_tr_b16): within
-// each 16-lane group, lane j points at row r0 + j/4, columns col0 + 4*(j%4)..+3,
-// and lane i receives column col0 + i of rows r0..r0+3.  fp32 reads element-wise.
-template <typename T, int D>
-__device__ __forceinline__ bf16x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, bf16*) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const int col = col0 + 4 * (i & 3);
-  const int chunk = col >> 3, byte = (col & 7) * 2;
-  const int r1 = 16 * s + 4 * h + (i >> 2), r2 = r1 + 8;
-  const char* base = reinterpret_cast<const char*>(lds);
-  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (bf16x4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r1, chunk) * 16 + byte));
-  const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (bf16x4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r2, chunk) * 16 + byte));
-  return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
-}
-template <typename T, int D>
-__device__ __forceinline__ f16x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, f16*) {
-  typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-  const int col = col0 + 4 * (i & 3);
-  const int chunk = col >> 3, byte = (col & 7) * 2;
-  const int r1 = 16 * s + 4 * h + (i >> 2), r2 = r1 + 8;
-  const char* base = reinterpret_cast<const char*>(lds);
-  const f16x4 v1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-      (h4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r1, chunk) * 16 + byte)));
-  const f16x4 v2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-      (h4 __attribute__((address_space(3)))*)(base + row_slot<T, D>(r2, chunk) * 16 + byte)));
-  return f16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
-}
-template <typename T, int D>
-__device__ __forceinline__ f32x8 frag_tr_rows(const u32x4* lds, int col0, int s, int h, int i, float*) {
-  const int col = col0 + i;
-  const int chunk = col >> 2, within = col & 3;
-  const float* base = reinterpret_cast<const float*>(lds);
-  f32x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = 16 * s + (e < 4 ? 4 * h + e : 8 + 4 * h + e - 4);
-    r[e] = base[row_slot<T, D>(row, chunk) * 4 + within];
-  }
-  return r;
-}
-
 // --- 16x16x32 matrix-core helpers ---------------------------------------------
 // v_mfma_f32_16x16x32 (bf16 / fp16; fp32 as eight 16x16x4 steps over the same
 // registers).  Layout (checked on the hardware): A (16 x 32) lane l holds row l%16
@@ -357,101 +265,6 @@ __device__ __forceinline__ void row_store(const RowStage<T, D>& st, u32x4* lds, 
   }
 }
 
-// Group items: per thread kGPer items of 8 chunks.
-template <typename T, int D>
-struct GroupStage {
-  u32x4 v[TileCfg<T, D>::kGPer][8];
-};
-template <typename T, int D>
-__device__ __forceinline__ void group_offsets(int (*off)[8], const Geo& g, int tid) {
-  using C = TileCfg<T, D>;
-#pragma unroll
-  for (int i = 0; i < C::kGPer; ++i) {
-    const int kg = (tid + i * kTileThreads) / C::kCPR;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = group_row(kg & 7, e);
-      off[i][e] = (kg < 8 && r < g.T) ? member_offset(g, r) : -1;
-    }
-  }
-}
-template <typename T, int D>
-__device__ __forceinline__ void group_load(GroupStage<T, D>& st, const T* __restrict__ X, int base,
-                                           const int (*off)[8], int tid) {
-  using C = TileCfg<T, D>;
-#pragma unroll
-  for (int i = 0; i < C::kGPer; ++i) {
-    const int c = (tid + i * kTileThreads) % C::kCPR;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      st.v[i][e] = off[i][e] >= 0 ? *reinterpret_cast<const u32x4*>(X + (size_t)(base + off[i][e]) * D + c * C::kCE)
-                                  : u32x4{0, 0, 0, 0};
-  }
-}
-
-// 8 tokens x one chunk -> transposed rows.  The stored element type is the
-// source type, except that bf16 sources can be stored as fp16 (exact for values
-// in the fp16 normal range; used for the operand of the fp16 P.V product).
-__device__ __forceinline__ uint32_t bf16_half(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
-
-__device__ __forceinline__ void transpose_store(u32x4* lds_t, const u32x4 (&v)[8], int kg, int c, bf16*, bf16*) {
-  using C = TileCfg<bf16, 64>;  // the transposed row geometry depends only on the element size
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {            // element m of the chunk -> row d = 8c + m
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)            // positions 2j, 2j+1 of the group
-      w[j] = bf16_half(v[2 * j][m >> 1], m & 1) | (bf16_half(v[2 * j + 1][m >> 1], m & 1) << 16);
-    const int d = 8 * c + m;
-    lds_t[d * C::kTR + (kg ^ ((d ^ (d >> C::kTLog)) & (C::kTR - 1)))] = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-__device__ __forceinline__ void transpose_store(u32x4* lds_t, const u32x4 (&v)[8], int kg, int c, bf16*, f16*) {
-  using C = TileCfg<f16, 64>;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f16 a = (f16)bf16_bits_to_f32(bf16_half(v[2 * j][m >> 1], m & 1));
-      const f16 b = (f16)bf16_bits_to_f32(bf16_half(v[2 * j + 1][m >> 1], m & 1));
-      w[j] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-    }
-    const int d = 8 * c + m;
-    lds_t[d * C::kTR + (kg ^ ((d ^ (d >> C::kTLog)) & (C::kTR - 1)))] = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-__device__ __forceinline__ void transpose_store(u32x4* lds_t, const u32x4 (&v)[8], int kg, int c, float*, float*) {
-  using C = TileCfg<float, 64>;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int d = 4 * c + m;
-    const int f = (d ^ (d >> C::kTLog)) & (C::kTR - 1);
-    lds_t[d * C::kTR + ((2 * kg) ^ f)] = u32x4{v[0][m], v[1][m], v[2][m], v[3][m]};
-    lds_t[d * C::kTR + ((2 * kg + 1) ^ f)] = u32x4{v[4][m], v[5][m], v[6][m], v[7][m]};
-  }
-}
-// store group items transposed (lds_t, element type TO) and, if lds_r != nullptr,
-// row-major too (source type T)
-template <typename T, int D, typename TO = T>
-__device__ __forceinline__ void group_store(const GroupStage<T, D>& st, u32x4* lds_t, u32x4* lds_r, int tid) {
-  using C = TileCfg<T, D>;
-#pragma unroll
-  for (int i = 0; i < C::kGPer; ++i) {
-    const int it = tid + i * kTileThreads;
-    if (it < C::kGItems) {
-      const int kg = it / C::kCPR, c = it % C::kCPR;
-      transpose_store(lds_t, st.v[i], kg, c, (T*)nullptr, (TO*)nullptr);
-      if (lds_r != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lds_r[row_slot<T, D>(group_row(kg, e), c)] = st.v[i][e];
-      }
-    }
-  }
-}
-
-// 4 fp32 values -> output row (16 bytes fp32, or 8 bytes bf16 rounded to nearest even)
 __device__ __forceinline__ void store4(void* base, size_t off, int out_f32, float v0, float v1, float v2, float v3) {
   if (out_f32) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off) = f32x4{v0, v1, v2, v3};
