@@ -60,6 +60,8 @@ def _load():
     L.dsa_predict.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.dsa_select.restype = ctypes.c_int
     L.dsa_select.argtypes = [sp, vp, vp, i32, vp, vp]
+    L.dsa_predict_select.restype = ctypes.c_int
+    L.dsa_predict_select.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     L.dsa_attn_fwd.restype = ctypes.c_int
     L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
     L.dsa_attn_fwd_workspace_bytes.restype = sz
@@ -178,6 +180,24 @@ def select(S: torch.Tensor, k: torch.Tensor, kmax: int, layout: Layout, d: int =
     idx = out if out is not None else torch.empty(B, H, layout.NB, kmax, device=S.device, dtype=torch.int32)
     _check(_L().dsa_select(ctypes.byref(sh), _ptr(S), _ptr(k), kmax, _ptr(idx), _stream()))
     return idx
+
+
+def predict_select(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, k: torch.Tensor, kmax: int,
+                   layout: Layout, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Predictor and top-k selection without the score matrix: returns (Qbar, Kbar, idx)."""
+    _dev(Q, K, Wq, Wk, k)
+    sh = _shape(Q, layout)
+    B, H = Q.shape[:2]
+    r = Wq.shape[-1]
+    if out is None:
+        Qbar = torch.empty(B, H, layout.NB, r, device=Q.device, dtype=torch.float32)
+        Kbar = torch.empty_like(Qbar)
+        idx = torch.empty(B, H, layout.NB, kmax, device=Q.device, dtype=torch.int32)
+    else:
+        Qbar, Kbar, idx = out
+    _check(_L().dsa_predict_select(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(k), kmax,
+                                   _ptr(Qbar), _ptr(Kbar), _ptr(idx), _stream()))
+    return Qbar, Kbar, idx
 
 
 def fwd_workspace_bytes(Q: torch.Tensor, layout: Layout) -> int:

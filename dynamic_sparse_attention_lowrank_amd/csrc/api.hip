@@ -109,6 +109,27 @@ dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q, const v
   return hip_status(launch_predict(a, dv.io_f32, dv.d, stream));
 }
 
+dsa_status dsa_predict_select(const dsa_shape* shape, int32_t r, const void* Q, const void* K, const void* Wq,
+                              const void* Wk, const int32_t* k, int32_t kmax, float* Qbar, float* Kbar, int32_t* idx,
+                              hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (r < 1 || r > 64) return DSA_ERR_RANK;
+  if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
+  if (dv.BH == 0) return DSA_OK;
+  if (!Q || !K || !Wq || !Wk || !Qbar || !Kbar || !k || !idx) return DSA_ERR_NULL;
+  PredictArgs a;
+  a.Q = Q; a.K = K; a.Wq = Wq; a.Wk = Wk;
+  a.Qbar = Qbar; a.Kbar = Kbar; a.S = nullptr;
+  a.g = dv.g; a.B = shape->B; a.H = shape->H; a.r = r;
+  hipError_t e = launch_pool_project(a, dv.io_f32, dv.d, stream);
+  if (e != hipSuccess) return hip_status(e);
+  FusedSelectArgs f;
+  f.Qbar = Qbar; f.Kbar = Kbar; f.kvec = k; f.kmax = kmax; f.idx = idx; f.NB = dv.g.NB; f.BH = dv.BH; f.r = r;
+  return hip_status(launch_fused_select(f, stream));
+}
+
 dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, int32_t kmax, int32_t* idx,
                       hipStream_t stream) {
   Derived dv;

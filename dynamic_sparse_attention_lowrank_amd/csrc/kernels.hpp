@@ -53,6 +53,20 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
+struct FusedSelectArgs {
+  const float* Qbar;
+  const float* Kbar;
+  const int32_t* kvec;
+  int kmax;
+  int32_t* idx;
+  int NB;
+  int BH;
+  int r;
+};
+hipError_t launch_fused_select(const FusedSelectArgs& a, hipStream_t s);
+// pooled features only (the first half of launch_predict)
+hipError_t launch_pool_project(const PredictArgs& a, int io_f32, int d, hipStream_t s);
+
 struct BwdArgs {
   const void* Q;
   const void* K;

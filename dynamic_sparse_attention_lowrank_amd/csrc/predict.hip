@@ -113,10 +113,13 @@ hipError_t launch_pool(const PredictArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_pool_project(const PredictArgs& a, int io_f32, int d, hipStream_t s) {
+  if (io_f32) return d == 64 ? launch_pool<float, 64>(a, s) : launch_pool<float, 128>(a, s);
+  return d == 64 ? launch_pool<bf16, 64>(a, s) : launch_pool<bf16, 128>(a, s);
+}
+
 hipError_t launch_predict(const PredictArgs& a, int io_f32, int d, hipStream_t s) {
-  hipError_t e;
-  if (io_f32) e = d == 64 ? launch_pool<float, 64>(a, s) : launch_pool<float, 128>(a, s);
-  else e = d == 64 ? launch_pool<bf16, 64>(a, s) : launch_pool<bf16, 128>(a, s);
+  hipError_t e = launch_pool_project(a, io_f32, d, s);
   if (e != hipSuccess) return e;
   const int NB = a.g.NB;
   dim3 grid((NB + kScoreCols - 1) / kScoreCols, (NB + kScoreRows - 1) / kScoreRows, a.B * a.H);

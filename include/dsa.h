@@ -112,6 +112,20 @@ DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int3
                       int32_t* idx, hipStream_t stream);
 
 /*
+ * dsa_predict_select -- dsa_predict followed by dsa_select without the score
+ *   matrix (the next step after the predictor and the selector: the selector
+ *   computes each row's scores on the fly and keeps only the top k).
+ *   Arguments mean what they mean for dsa_predict and dsa_select; Qbar and Kbar
+ *   are written as by dsa_predict, idx as by dsa_select, and no [B,H,NB,NB]
+ *   array is read or written.  The scores are the same float32 operations in the
+ *   same order as dsa_predict's, so idx is identical to dsa_predict + dsa_select.
+ *   Errors: those of dsa_predict (without S) and of dsa_select.
+ */
+DSA_API dsa_status dsa_predict_select(const dsa_shape* shape, int32_t r, const void* Q, const void* K,
+                                      const void* Wq, const void* Wk, const int32_t* k, int32_t kmax,
+                                      float* Qbar, float* Kbar, int32_t* idx, hipStream_t stream);
+
+/*
  * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
  * this shape (0 on invalid arguments): 2*B*H*NB*d*64 elements of 2 bytes (bf16
  * io) or 4 bytes (fp32 io).  dsa_attn_fwd first rewrites every key block's K

@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = set(declared_functions())
-    assert {"dsa_predict", "dsa_select", "dsa_attn_fwd", "dsa_attn_bwd", "dsa_attn_bwd_workspace_bytes",
-            "dsa_status_string", "dsa_version"} <= names
+    assert {"dsa_predict", "dsa_select", "dsa_predict_select", "dsa_attn_fwd", "dsa_attn_bwd",
+            "dsa_attn_bwd_workspace_bytes", "dsa_status_string", "dsa_version"} <= names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -69,6 +69,11 @@ def test_entry_point_validation(L):
     assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 0, FAKE, None) == 4
     assert lib.dsa_select(ctypes.byref(sh), FAKE, FAKE, 17, FAKE, None) == 4      # kmax > NB = 16
     assert lib.dsa_select(ctypes.byref(sh), None, FAKE, 4, FAKE, None) == 1
+    ps = lambda shp, r, kmax, *p: lib.dsa_predict_select(shp, r, *p[:5], kmax, *p[5:], None)
+    assert ps(ctypes.byref(sh), 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == 9
+    assert ps(ctypes.byref(sh), 16, 17, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == 4
+    assert ps(ctypes.byref(sh), 16, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE) == 1
+    assert ps(None, 16, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == 1
     fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
     assert fneed == 2 * (1 * 2 * 16 * 64 * 64 * 4)                              # K and V^T: 2*B*H*NB*d*64 fp32
     fw = [FAKE, fneed, None]
