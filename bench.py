@@ -2,8 +2,9 @@
 """Benchmark: one training step of DSV-style dynamic block-sparse attention on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic video tokens:
-predictor scores -> top-k block selection -> block-sparse attention forward ->
-backward (D + reverse index, dK/dV, dQ).  Workload: B=1, H=24, d=128, latent
+pooled low-rank predictor -> top-k block selection (scores formed per row, no
+score matrix; --score-matrix times the two-step path) -> block-sparse attention
+forward -> backward (D + reverse index, dK/dV, dQ).  Workload: B=1, H=24, d=128, latent
 16x32x64 = 32,768 tokens, 1x8x8 tiles (512 blocks), rank 16, 10 % of the blocks
 kept (k = 52), bf16 inputs.  Inputs are resident in HBM before timing starts.
 
@@ -40,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="train_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--score-matrix", action="store_true",
+                    help="predict (writes the NB x NB scores) then select, instead of the fused entry point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one int32 bitwise-not of this many MiB (a plain streaming "
                          "kernel of known traffic, the HBM counter calibration)")
@@ -160,7 +163,7 @@ def main():
     f32 = torch.float32
     Qbar = torch.empty(B, H, NB, r, device=dev, dtype=f32)
     Kbar = torch.empty_like(Qbar)
-    S = torch.empty(B, H, NB, NB, device=dev, dtype=f32)
+    S = torch.empty(B, H, NB, NB, device=dev, dtype=f32) if args.score_matrix else None
     idx = torch.empty(B, H, NB, kmax, device=dev, dtype=torch.int32)
     O = torch.empty(B, H, N, d, device=dev, dtype=f32)
     LSE = torch.empty(B, H, N, device=dev, dtype=f32)
@@ -172,13 +175,20 @@ def main():
     Q, K, V, dO, Wq, Wk = (x[n] for n in ("Q", "K", "V", "dO", "Wq", "Wk"))
 
     phases = ["predict", "select", "fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq"]
+    if not args.score_matrix:
+        phases[0:2] = ["predict_select", "-"]
 
     def step(ev=None):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
-        dsa.predict(Q, K, Wq, Wk, lay, out=(Qbar, Kbar, S))
-        rec(1)
-        dsa.select(S, kdev, kmax, lay, d=d, out=idx)
+        if args.score_matrix:
+            dsa.predict(Q, K, Wq, Wk, lay, out=(Qbar, Kbar, S))
+            rec(1)
+            dsa.select(S, kdev, kmax, lay, d=d, out=idx)
+        else:
+            # pooled predictor, then per-row scores + top-k without the score matrix
+            dsa.predict_select(Q, K, Wq, Wk, kdev, kmax, lay, out=(Qbar, Kbar, idx))
+            rec(1)
         rec(2)
         dsa.attn_fwd(Q, K, V, idx, kdev, lay, out=(O, LSE), workspace=fws)
         rec(3)
@@ -245,12 +255,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: one attention layer, training step (predict+select+fwd+bwd)",
+                   "predictor": "two-step (score matrix)" if args.score_matrix else "fused predict+select",
                    "B": B, "H": H, "d": d, "latent": list(wl.latent), "tokens": N, "tile": list(wl.tile),
                    "blocks": NB, "rank": r, "k": kmax, "keep_percent": list(wl.keep_percent)},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "fwd": {"ms": round(phase_ms["fwd"], 4), "tflops": round(fwd_tflops, 2),
                 "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2)},
-        "phase_ms": {p: round(v, 4) for p, v in phase_ms.items()},
+        "phase_ms": {p: round(v, 4) for p, v in phase_ms.items() if p != "-"},
         "event_ms_per_step": round(span_ms, 4),
         "counted_flop": {"fwd": flop_fwd, "bwd": flop_bwd, "pairs": pairs},
         "roofline": roofline,
@@ -273,6 +284,10 @@ def _kernel_label(raw: str) -> str:
     name = m.group(1)
     tail = raw[m.end():]
     args = []
+    if name in ("fused_select_kernel", "select_kernel"):     # <slots per lane[, rank, exact rank]>
+        ints = re.findall(r"Li(\d+)E", tail[:40]) or re.findall(r"(\d+)", tail[:tail.find(">") + 1])
+        exact = "Lb1E" in tail[:40] or "true>" in tail[:40]
+        return f"{name}<{','.join(ints + (['exact'] if exact else []))}>"
     if tail.startswith("I") or tail.startswith("<"):
         if "DF16b" in tail[:8] or "__bf16" in tail[:12]:
             args.append("bf16")

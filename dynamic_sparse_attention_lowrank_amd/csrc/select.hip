@@ -7,11 +7,11 @@
 //
 // One wave per row.  Scores become order-preserving 32-bit keys (canonical +0,
 // NaN lowest).  The (k-1)-th largest key T is found by a 32-step bitwise search
-// (each step counts keys >= candidate with one compare + ballot + popcount per
-// register slot, so the counting runs on the scalar unit), then a single
-// ascending sweep emits: own block, keys > T, and the lowest-index keys == T until
-// k are taken.  Rows of up to 8192 blocks live in registers; longer rows are
-// re-read from memory on each step (L2-resident).
+// (each step counts the keys >= candidate: ballot + scalar popcount per register
+// slot on rows of up to 1024 blocks, per-lane vector counts and one DPP wave sum on
+// longer rows), then a single ascending sweep emits: own block, keys > T, and the
+// lowest-index keys == T until k are taken.  Rows of up to 8192 blocks live in
+// registers; longer rows are re-read from memory on each step (L2-resident).
 //
 // The fused variant (dsa_predict_select) computes each row's scores from the
 // pooled features instead of reading a stored score matrix (bit-identical scores),
@@ -20,11 +20,33 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <utility>
+
 namespace dsa {
 
 namespace {
 
 constexpr int kWaves = 4;
+
+// The lane id behind an empty asm: each phase derives its per-slot block ids from
+// its own copy, so the compiler cannot keep one id register per slot alive from the
+// loads through the search to the sweep (64-128 extra VGPRs on long rows).
+__device__ __forceinline__ int fresh_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
+// Sum of an int over the 64 lanes: DPP within each 16-lane row (quad swaps, then
+// half-row and row mirrors leave every lane of a row holding the row's sum), then
+// the four row sums on the scalar unit.  Needs all lanes active.
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);   // row_half_mirror
+  v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true);   // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -43,26 +65,36 @@ struct Row {
   int NB, tau, lane, nslots;
   uint32_t key[SLOTS > 0 ? SLOTS : 1];
 
-  __device__ __forceinline__ uint32_t load(int i) const {
-    const int j = 64 * i + lane;
-    return (j < NB && j != tau) ? order_key(s[j]) : 0u;
+  __device__ __forceinline__ uint32_t load(int i, int l) const {
+    const int j = 64 * i + l;
+    const uint32_t key = order_key(s[j < NB ? j : NB - 1]);   // clamped: no branch per slot
+    return (j < NB && j != tau) ? key : 0u;
   }
+  __device__ __forceinline__ uint32_t load(int i) const { return load(i, lane); }
   __device__ __forceinline__ void init() {
     if constexpr (SLOTS > 0) {
+      const int l = fresh_lane(lane);
 #pragma unroll
-      for (int i = 0; i < SLOTS; ++i) key[i] = load(i);
+      for (int i = 0; i < SLOTS; ++i) key[i] = load(i, l);
     }
   }
   // number of candidates with key >= t (t >= 1)
+  // Short rows: ballot + scalar popcount per slot.  Long rows: per-lane counts on
+  // the vector unit and one wave sum per call (with ballots the compiler keeps one
+  // mask or partial count per slot live and spills them).
   __device__ __forceinline__ int count_ge(uint32_t t) const {
     int cnt = 0;
-    if constexpr (SLOTS > 0) {
+    if constexpr (SLOTS > 0 && SLOTS <= 16) {
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) cnt += __popcll(ballot(key[i] >= t));
+      return cnt;
+    } else if constexpr (SLOTS > 16) {
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) cnt += key[i] >= t ? 1 : 0;
     } else {
-      for (int i = 0; i < nslots; ++i) cnt += __popcll(ballot(load(i) >= t));
+      for (int i = 0; i < nslots; ++i) cnt += load(i) >= t ? 1 : 0;
     }
-    return cnt;
+    return wave_sum(cnt);
   }
   __device__ __forceinline__ uint32_t at(int i) const {
     if constexpr (SLOTS > 0) return key[i];
@@ -71,11 +103,14 @@ struct Row {
 };
 
 template <typename R>
-__device__ __forceinline__ void sweep_slot(const R& rw, int i, uint32_t T, int kp, int need_eq,
-                                           int& taken, int& eq_seen, int32_t* __restrict__ out, int kmax) {
-  const int j = 64 * i + rw.lane;
+__device__ __forceinline__ void sweep_slot(const R& rw, int i, int l, bool own_lane, uint32_t T, int kp,
+                                           int need_eq, int& taken, int& eq_seen, int32_t* __restrict__ out,
+                                           int kmax) {
+  const int j = 64 * i + l;
   const uint32_t key = rw.at(i);
-  const bool own = (j == rw.tau);
+  // own block: a uniform slot test and one lane test (a per-slot compare of j with
+  // tau would be merged with the one in init and keep a mask per slot alive)
+  const bool own = (i == (rw.tau >> 6)) && own_lane;
   const bool eq = kp > 0 && key == T;                  // T >= 1 whenever kp > 0
   const uint64_t eqm = ballot(eq);
   const bool pick = own || (kp > 0 && key > T) || (eq && eq_seen + lanes_below(eqm) < need_eq);
@@ -104,11 +139,13 @@ __device__ __forceinline__ void select_row(const R& rw, int kp, int k, int32_t* 
   }
 
   int taken = 0, eq_seen = 0;
+  const int l = fresh_lane(rw.lane);
+  const bool own_lane = l == (rw.tau & 63);
   if constexpr (SLOTS > 0) {
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) sweep_slot(rw, i, T, kp, need_eq, taken, eq_seen, out, kmax);
+    for (int i = 0; i < SLOTS; ++i) sweep_slot(rw, i, l, own_lane, T, kp, need_eq, taken, eq_seen, out, kmax);
   } else {
-    for (int i = 0; i < rw.nslots; ++i) sweep_slot(rw, i, T, kp, need_eq, taken, eq_seen, out, kmax);
+    for (int i = 0; i < rw.nslots; ++i) sweep_slot(rw, i, l, own_lane, T, kp, need_eq, taken, eq_seen, out, kmax);
   }
   for (int p = k + rw.lane; p < kmax; p += 64) out[p] = -1;
 }
@@ -116,7 +153,7 @@ __device__ __forceinline__ void select_row(const R& rw, int kp, int k, int32_t* 
 template <int SLOTS>
 __global__ __launch_bounds__(64 * kWaves) void select_kernel(SelectArgs a) {
   const int lane = threadIdx.x & 63;
-  const int rowid = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int rowid = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (rowid >= a.BH * a.NB) return;                     // whole wave exits together
   const int NB = a.NB;
   const int bh = rowid / NB;
@@ -151,48 +188,62 @@ hipError_t launch_sel(const SelectArgs& a, hipStream_t s) {
 // (s = sum over c < RM of fma(Qbar[tau][c], Kbar[j][c], s), zero beyond r), so the
 // selection is identical to dsa_predict + dsa_select without the NB x NB matrix.
 // The four waves of a work-group share each Kbar row through the L1 cache.
-template <int SLOTS, int RM>
-struct FusedRow {
+// EXACT: r == RM (a multiple of 4): 16-byte loads of the Kbar rows, no per-term
+// tests.  Otherwise r < RM or r % 4 != 0: scalar loads, terms c >= r are zero.
+template <int RM, bool EXACT>
+struct PooledRow {
   const float* __restrict__ kb;      // Kbar of the head, [NB][r]
   float qv[RM];                      // Qbar row (zero beyond r)
-  int r, NB, tau, lane, nslots;
-  uint32_t key[SLOTS > 0 ? SLOTS : 1];
+  int r, NB, tau;
 
-  __device__ __forceinline__ uint32_t load(int i) const {
-    const int j = 64 * i + lane;
-    if (j >= NB || j == tau) return 0u;
-    const float* kr = kb + (size_t)j * r;
+  __device__ __forceinline__ uint32_t key(int i, int l) const {
+    const int j = 64 * i + l;
+    const float* kr = kb + (size_t)(j < NB ? j : NB - 1) * r;
     float s = 0.f;
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int c = 0; c < RM; ++c) s = fmaf(qv[c], c < r ? kr[c] : 0.f, s);
-    return order_key(s);
-  }
-  __device__ __forceinline__ void init() {
-    if constexpr (SLOTS > 0) {
-#pragma unroll
-      for (int i = 0; i < SLOTS; ++i) key[i] = load(i);
-    }
-  }
-  __device__ __forceinline__ int count_ge(uint32_t t) const {
-    int cnt = 0;
-    if constexpr (SLOTS > 0) {
-#pragma unroll
-      for (int i = 0; i < SLOTS; ++i) cnt += __popcll(ballot(key[i] >= t));
+      for (int c = 0; c < RM; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(kr + c);
+        s = fmaf(qv[c], v.x, s);
+        s = fmaf(qv[c + 1], v.y, s);
+        s = fmaf(qv[c + 2], v.z, s);
+        s = fmaf(qv[c + 3], v.w, s);
+      }
     } else {
-      for (int i = 0; i < nslots; ++i) cnt += __popcll(ballot(load(i) >= t));
+#pragma unroll
+      for (int c = 0; c < RM; ++c) s = fmaf(qv[c], c < r ? kr[c] : 0.f, s);
     }
-    return cnt;
+    return (j < NB && j != tau) ? order_key(s) : 0u;
   }
-  __device__ __forceinline__ uint32_t at(int i) const {
-    if constexpr (SLOTS > 0) return key[i];
-    else return load(i);
+  // all slots of a register-held row, expanded at compile time (a loop this long is
+  // not unrolled completely, and the key array would then live in scratch memory)
+  template <int... I>
+  __device__ __forceinline__ void fill_seq(uint32_t* key, int l, std::integer_sequence<int, I...>) const {
+    ((key[I] = this->key(I, l)), ...);
+  }
+  template <int SLOTS>
+  __device__ __forceinline__ void fill(uint32_t (&key)[SLOTS], int l) const {
+    fill_seq(key, l, std::make_integer_sequence<int, SLOTS>{});
   }
 };
 
-template <int SLOTS, int RM>
+// rows longer than 8192 blocks: scores recomputed on every pass
+template <int RM, bool EXACT>
+struct RecomputedRow {
+  PooledRow<RM, EXACT> p;
+  int tau, lane, nslots;
+  __device__ __forceinline__ int count_ge(uint32_t t) const {
+    int cnt = 0;
+    for (int i = 0; i < nslots; ++i) cnt += p.key(i, lane) >= t ? 1 : 0;
+    return wave_sum(cnt);
+  }
+  __device__ __forceinline__ uint32_t at(int i) const { return p.key(i, lane); }
+};
+
+template <int SLOTS, int RM, bool EXACT>
 __global__ __launch_bounds__(64 * kWaves) void fused_select_kernel(FusedSelectArgs a) {
   const int lane = threadIdx.x & 63;
-  const int rowid = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int rowid = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (rowid >= a.BH * a.NB) return;                     // whole wave exits together
   const int NB = a.NB;
   const int bh = rowid / NB;
@@ -201,47 +252,64 @@ __global__ __launch_bounds__(64 * kWaves) void fused_select_kernel(FusedSelectAr
   k = k < 1 ? 1 : (k > a.kmax ? a.kmax : k);
   int32_t* __restrict__ out = a.idx + (size_t)rowid * a.kmax;
 
-  FusedRow<SLOTS, RM> rw;
-  rw.kb = a.Kbar + (size_t)bh * NB * a.r;
-  const float* qb = a.Qbar + (size_t)rowid * a.r;
+  PooledRow<RM, EXACT> p;
+  p.kb = a.Kbar + (size_t)bh * NB * a.r;
+  // the Qbar row is the same for all lanes; read through a lane-dependent-looking
+  // address so it lands in VGPRs (up to 64 values would crowd the SGPRs)
+  const float* qb = a.Qbar + (size_t)rowid * a.r + fresh_lane(0);
 #pragma unroll
-  for (int c = 0; c < RM; ++c) rw.qv[c] = c < a.r ? qb[c] : 0.f;
-  rw.r = a.r;
-  rw.NB = NB;
-  rw.tau = tau;
-  rw.lane = lane;
-  rw.nslots = (NB + 63) / 64;
-  rw.init();
-  select_row<SLOTS>(rw, k - 1, k, out, a.kmax);
+  for (int c = 0; c < RM; ++c) p.qv[c] = c < a.r ? qb[c] : 0.f;
+  p.r = a.r;
+  p.NB = NB;
+  p.tau = tau;
+
+  if constexpr (SLOTS > 0) {
+    Row<SLOTS> rw;                 // keys only: the pooled row's scores, computed once
+    rw.s = nullptr;
+    rw.NB = NB;
+    rw.tau = tau;
+    rw.lane = lane;
+    rw.nslots = SLOTS;
+    p.fill(rw.key, fresh_lane(lane));
+    select_row<SLOTS>(rw, k - 1, k, out, a.kmax);
+  } else {
+    RecomputedRow<RM, EXACT> rw;
+    rw.p = p;
+    rw.tau = tau;
+    rw.lane = lane;
+    rw.nslots = (NB + 63) / 64;
+    select_row<0>(rw, k - 1, k, out, a.kmax);
+  }
 }
 
-template <int SLOTS, int RM>
+template <int SLOTS, int RM, bool EXACT>
 hipError_t launch_fsel(const FusedSelectArgs& a, hipStream_t s) {
   const int rows = a.BH * a.NB;
   const int grid = (rows + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((fused_select_kernel<SLOTS, RM>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+  hipLaunchKernelGGL((fused_select_kernel<SLOTS, RM, EXACT>), dim3(grid), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
-template <int RM>
+template <int RM, bool EXACT>
 hipError_t launch_fsel_rm(const FusedSelectArgs& a, hipStream_t s) {
   const int slots = (a.NB + 63) / 64;
-  if (slots <= 1) return launch_fsel<1, RM>(a, s);
-  if (slots <= 2) return launch_fsel<2, RM>(a, s);
-  if (slots <= 4) return launch_fsel<4, RM>(a, s);
-  if (slots <= 8) return launch_fsel<8, RM>(a, s);
-  if (slots <= 16) return launch_fsel<16, RM>(a, s);
-  if (slots <= 32) return launch_fsel<32, RM>(a, s);
-  if (slots <= 64) return launch_fsel<64, RM>(a, s);
-  if (slots <= 128) return launch_fsel<128, RM>(a, s);
-  return launch_fsel<0, RM>(a, s);
+  if (slots <= 1) return launch_fsel<1, RM, EXACT>(a, s);
+  if (slots <= 2) return launch_fsel<2, RM, EXACT>(a, s);
+  if (slots <= 4) return launch_fsel<4, RM, EXACT>(a, s);
+  if (slots <= 8) return launch_fsel<8, RM, EXACT>(a, s);
+  if (slots <= 16) return launch_fsel<16, RM, EXACT>(a, s);
+  if (slots <= 32) return launch_fsel<32, RM, EXACT>(a, s);
+  if (slots <= 64) return launch_fsel<64, RM, EXACT>(a, s);
+  if (slots <= 128) return launch_fsel<128, RM, EXACT>(a, s);
+  return launch_fsel<0, RM, EXACT>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_fused_select(const FusedSelectArgs& a, hipStream_t s) {
-  if (a.r <= 16) return launch_fsel_rm<16>(a, s);
-  if (a.r <= 32) return launch_fsel_rm<32>(a, s);
-  return launch_fsel_rm<64>(a, s);
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.Kbar) & 15) == 0;   // 16-byte row loads
+  if (aligned && a.r == 16) return launch_fsel_rm<16, true>(a, s);
+  if (aligned && a.r == 32) return launch_fsel_rm<32, true>(a, s);
+  return launch_fsel_rm<64, false>(a, s);                  // any other rank up to 64
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
