@@ -28,7 +28,9 @@ its reason in the design notes of this repository):
   padded with -1;
 * attention: exact softmax of (q . k) * scale over all keys of the kept blocks,
   scale = 1/sqrt(d), non-causal; LSE is a natural log;
-* backward: the block mask is held fixed (no gradient reaches the predictor).
+* backward: the block mask is held fixed (no gradient reaches the predictor);
+* predictor training (stage one, section 4): squared error of the scores against
+  the pooled attention logits, gradient for Wq and Wk only.
 
 Every array here is float64 (inputs are upcast exactly from their storage
 dtype).  Library primitives used as steps: matrix products, argsort/lexsort,
@@ -121,6 +123,70 @@ def predict_head(Q: np.ndarray, K: np.ndarray, Wq: np.ndarray, Wk: np.ndarray,
     Qbar = pooled_features(Q, Wq, members)
     Kbar = pooled_features(K, Wk, members)
     return Qbar, Kbar, block_scores(Qbar, Kbar)
+
+
+# ----------------------------------------------------------------------------
+# Predictor training (DSV page section 4, stage one: the predictor is trained
+# alongside the model so that it names the blocks that matter).  The page gives
+# no loss.  Reading: the predictor's scores estimate the pooled attention logits,
+# T[tau, j] = mean over query tokens i of tile tau and key tokens n of block j of
+# q_i . k_n (the quantity a full-rank predictor would give), and stage one
+# minimises the mean squared difference per (b, h):
+#     loss = (1 / NB^2) * sum over tau, j of (S[tau, j] - T[tau, j])^2.
+# Only the predictor weights receive a gradient.
+# ----------------------------------------------------------------------------
+def tile_means(X: np.ndarray, members: np.ndarray) -> np.ndarray:
+    """P[tau] = mean over the tokens of tile tau of X[n].  Returns [NB, d]."""
+    return np.asarray(X, dtype=np.float64)[members].mean(axis=1)
+
+
+def pooled_logits(Q: np.ndarray, K: np.ndarray, members: np.ndarray) -> np.ndarray:
+    """T[tau, j] = mean of q_i . k_n over i in tile tau, n in block j.
+
+    The mean of the pairwise dot products equals the dot product of the two
+    means (bilinearity), which is how it is evaluated here.  Returns [NB, NB].
+    """
+    return tile_means(Q, members) @ tile_means(K, members).T
+
+
+def predictor_loss_head(Q, K, Wq, Wk, members: np.ndarray) -> float:
+    """Stage-one loss of one (b, h): mean over all (tau, j) of (S - T)^2."""
+    _, _, S = predict_head(Q, K, Wq, Wk, members)
+    E = S - pooled_logits(Q, K, members)
+    return float((E * E).sum() / E.size)
+
+
+def predictor_grad_head(Q, K, Wq, Wk, members: np.ndarray):
+    """(loss, dloss/dWq, dloss/dWk) of one (b, h); gradients [d, r].
+
+    Chain rule through S = Qbar Kbar^T and Qbar = (tile mean of Q) Wq (the mean
+    of the projections is the projection of the mean, so dQbar/dWq involves
+    the tile means), likewise for Kbar.
+    """
+    Qbar, Kbar, S = predict_head(Q, K, Wq, Wk, members)
+    E = S - pooled_logits(Q, K, members)
+    loss = float((E * E).sum() / E.size)
+    dS = 2.0 * E / E.size                              # d loss / d S
+    dQbar = dS @ Kbar                                  # [NB, r]
+    dKbar = dS.T @ Qbar
+    dWq = tile_means(Q, members).T @ dQbar             # [d, r]
+    dWk = tile_means(K, members).T @ dKbar
+    return loss, dWq, dWk
+
+
+def predictor_grad(Q, K, Wq, Wk, geom: "Geometry"):
+    """loss [B,H] per (b, h); dWq, dWk [H,d,r] = gradients of the sum of all losses."""
+    members = geom.members()
+    B, H = Q.shape[:2]
+    loss = np.zeros((B, H))
+    dWq = np.zeros(np.shape(Wq))
+    dWk = np.zeros(np.shape(Wk))
+    for h in range(H):
+        for b in range(B):
+            loss[b, h], gq, gk = predictor_grad_head(Q[b, h], K[b, h], Wq[h], Wk[h], members)
+            dWq[h] += gq
+            dWk[h] += gk
+    return loss, dWq, dWk
 
 
 # ----------------------------------------------------------------------------

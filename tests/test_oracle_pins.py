@@ -146,6 +146,105 @@ def test_predictor_homogeneity(tiny):
     assert np.abs(St - S.T).max() <= 1e-12 * np.abs(S).max()
 
 
+# ---------------------------------------------------------------- predictor training
+def _small_train_case(seed=5, d=6, r=3):
+    """Tiny geometry (NB = 16 tiles of 4 tokens) with random fp64 Q, K, Wq, Wk."""
+    geom = Geometry(2, 4, 8, 1, 2, 2)
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((geom.N, d))
+    K = rng.standard_normal((geom.N, d)) + 0.5 * Q          # correlated, as attention inputs are
+    Wq = rng.standard_normal((d, r)) / math.sqrt(d)
+    Wk = rng.standard_normal((d, r)) / math.sqrt(d)
+    return geom, geom.members(), Q, K, Wq, Wk
+
+
+def test_pooled_logits_bruteforce_pairs():
+    """T-1: T[tau, j] is the mean over all (query token, key token) pairs of q_i . k_n,
+    computed pair by pair."""
+    geom, mem, Q, K, _, _ = _small_train_case()
+    T = oracle.pooled_logits(Q, K, mem)
+    for tau in range(geom.NB):
+        for j in (0, 3, 9, 15):
+            acc = sum(float(Q[i] @ K[n]) for i in mem[tau] for n in mem[j])
+            assert abs(T[tau, j] - acc / (len(mem[tau]) * len(mem[j]))) < 1e-12 * max(1.0, abs(acc))
+
+
+def test_predictor_loss_special_cases():
+    """T-2: Wq = 0 gives S = 0, so the loss is the mean of T^2; a full-rank
+    predictor with Wq Wk^T = I reproduces T exactly (loss 0, gradients 0)."""
+    geom, mem, Q, K, Wq, Wk = _small_train_case(d=6, r=6)
+    T = oracle.pooled_logits(Q, K, mem)
+    loss0 = oracle.predictor_loss_head(Q, K, np.zeros_like(Wq), Wk, mem)
+    assert abs(loss0 - (T ** 2).mean()) <= 1e-12 * (T ** 2).mean()
+    A = np.random.default_rng(1).standard_normal((6, 6)) + 3 * np.eye(6)
+    loss, gq, gk = oracle.predictor_grad_head(Q, K, A, np.linalg.inv(A).T, mem)
+    assert loss < 1e-24 and np.abs(gq).max() < 1e-12 and np.abs(gk).max() < 1e-12
+
+
+def test_predictor_loss_quadratic_in_scale():
+    """T-3: S is linear in Wq, so loss(c Wq) = a c^2 - 2 b c + loss(0) with
+    a = mean(S^2), b = mean(S T) at c = 1."""
+    geom, mem, Q, K, Wq, Wk = _small_train_case()
+    _, _, S = oracle.predict_head(Q, K, Wq, Wk, mem)
+    T = oracle.pooled_logits(Q, K, mem)
+    a, b, t = (S * S).mean(), (S * T).mean(), (T * T).mean()
+    for c in (-1.5, 0.3, 2.0):
+        got = oracle.predictor_loss_head(Q, K, c * Wq, Wk, mem)
+        assert abs(got - (a * c * c - 2 * b * c + t)) <= 1e-12 * max(1.0, t)
+
+
+def test_predictor_grad_finite_differences():
+    """T-4: the analytic gradient of the oracle equals central differences of
+    its loss, entry by entry, for Wq and Wk."""
+    geom, mem, Q, K, Wq, Wk = _small_train_case()
+    _, gq, gk = oracle.predictor_grad_head(Q, K, Wq, Wk, mem)
+    h = 1e-6
+    for W, G, which in ((Wq, gq, 0), (Wk, gk, 1)):
+        for e in range(W.shape[0]):
+            for c in range(W.shape[1]):
+                Wp, Wm = W.copy(), W.copy()
+                Wp[e, c] += h
+                Wm[e, c] -= h
+                args_p = (Wp, Wk) if which == 0 else (Wq, Wp)
+                args_m = (Wm, Wk) if which == 0 else (Wq, Wm)
+                fd = (oracle.predictor_loss_head(Q, K, *args_p, mem) -
+                      oracle.predictor_loss_head(Q, K, *args_m, mem)) / (2 * h)
+                assert abs(fd - G[e, c]) <= 1e-7 * max(1.0, np.abs(G).max()), (which, e, c)
+
+
+def test_predictor_grad_vanishes_at_least_squares_optimum():
+    """T-5: for a fixed Wk the loss is a least-squares problem in Wq.  Its
+    minimiser, Wq* = lstsq(Kbar-basis B = Pk Wk, Pk)^T (so that Wq* B^T is the
+    projection of Pk^T onto the span of B), is computed by numpy's least squares;
+    the oracle's dWq vanishes there and the loss does not drop nearby."""
+    geom, mem, Q, K, Wq, Wk = _small_train_case(seed=9)
+    Pk = K[mem].mean(axis=1)
+    Bm = Pk @ Wk
+    Wq_opt = np.linalg.lstsq(Bm, Pk, rcond=None)[0].T
+    loss_opt, gq, _ = oracle.predictor_grad_head(Q, K, Wq_opt, Wk, mem)
+    _, gq_rand, _ = oracle.predictor_grad_head(Q, K, Wq, Wk, mem)
+    assert np.abs(gq).max() <= 1e-10 * np.abs(gq_rand).max()
+    rng = np.random.default_rng(3)
+    for _ in range(5):
+        pert = Wq_opt + 1e-3 * rng.standard_normal(Wq_opt.shape)
+        assert oracle.predictor_loss_head(Q, K, pert, Wk, mem) >= loss_opt
+
+
+def test_predictor_grad_sums_over_batch(tiny):
+    """T-6: the whole-tensor helper sums the per-(b, h) gradients over b."""
+    wl, x = tiny
+    geom = geom_of(wl)
+    mem = geom.members()
+    Q = np.concatenate([x["Q"], 0.5 * x["K"]], axis=0)     # B = 2
+    K = np.concatenate([x["K"], x["Q"]], axis=0)
+    loss, gq, gk = oracle.predictor_grad(Q, K, x["Wq"], x["Wk"], geom)
+    for h in range(wl.H):
+        parts = [oracle.predictor_grad_head(Q[b, h], K[b, h], x["Wq"][h], x["Wk"][h], mem) for b in range(2)]
+        assert np.allclose(loss[:, h], [p[0] for p in parts], rtol=0, atol=0)
+        assert np.abs(gq[h] - parts[0][1] - parts[1][1]).max() <= 1e-15 * np.abs(gq[h]).max()
+        assert np.abs(gk[h] - parts[0][2] - parts[1][2]).max() <= 1e-15 * np.abs(gk[h]).max()
+
+
 # ---------------------------------------------------------------- selection
 def brute_force_select(scores, tau, k):
     """Max-sum subset of k-1 other blocks; equal sums -> lexicographically smallest."""
