@@ -26,6 +26,7 @@ import torch
 __all__ = [
     "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
     "bwd_workspace_bytes", "fwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
+    "predict_select", "predictor_grad", "predictor_grad_workspace_bytes",
 ]
 
 F32 = 0
@@ -62,6 +63,10 @@ def _load():
     L.dsa_select.argtypes = [sp, vp, vp, i32, vp, vp]
     L.dsa_predict_select.restype = ctypes.c_int
     L.dsa_predict_select.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    L.dsa_predictor_grad_workspace_bytes.restype = sz
+    L.dsa_predictor_grad_workspace_bytes.argtypes = [sp]
+    L.dsa_predictor_grad.restype = ctypes.c_int
+    L.dsa_predictor_grad.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_attn_fwd.restype = ctypes.c_int
     L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
     L.dsa_attn_fwd_workspace_bytes.restype = sz
@@ -198,6 +203,33 @@ def predict_select(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch
     _check(_L().dsa_predict_select(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(k), kmax,
                                    _ptr(Qbar), _ptr(Kbar), _ptr(idx), _stream()))
     return Qbar, Kbar, idx
+
+
+def predictor_grad_workspace_bytes(Q: torch.Tensor, layout: Layout) -> int:
+    sh = _shape(Q, layout)
+    return int(_L().dsa_predictor_grad_workspace_bytes(ctypes.byref(sh)))
+
+
+def predictor_grad(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, layout: Layout,
+                   out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Stage-one predictor loss and weight gradients: returns (loss [B,H], dWq [H,d,r], dWk [H,d,r]), fp32."""
+    _dev(Q, K, Wq, Wk)
+    sh = _shape(Q, layout)
+    B, H = Q.shape[:2]
+    r = Wq.shape[-1]
+    if out is None:
+        loss = torch.empty(B, H, device=Q.device, dtype=torch.float32)
+        dWq = torch.empty(Wq.shape, device=Q.device, dtype=torch.float32)
+        dWk = torch.empty(Wk.shape, device=Q.device, dtype=torch.float32)
+    else:
+        loss, dWq, dWk = out
+    if workspace is None:
+        need = int(_L().dsa_predictor_grad_workspace_bytes(ctypes.byref(sh)))
+        workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
+    _check(_L().dsa_predictor_grad(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(loss), _ptr(dWq),
+                                   _ptr(dWk), _ptr(workspace), workspace.numel(), _stream()))
+    return loss, dWq, dWk
 
 
 def fwd_workspace_bytes(Q: torch.Tensor, layout: Layout) -> int:

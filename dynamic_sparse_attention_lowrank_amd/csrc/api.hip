@@ -130,6 +130,38 @@ dsa_status dsa_predict_select(const dsa_shape* shape, int32_t r, const void* Q, 
   return hip_status(launch_fused_select(f, stream));
 }
 
+size_t dsa_predictor_grad_workspace_bytes(const dsa_shape* shape) {
+  Derived dv;
+  if (derive(shape, &dv) != DSA_OK) return 0;
+  return predictor_grad_workspace_bytes(dv.BH, shape->H, dv.g.NB, dv.d);
+}
+
+dsa_status dsa_predictor_grad(const dsa_shape* shape, int32_t r, const void* Q, const void* K, const void* Wq,
+                              const void* Wk, float* loss, float* dWq, float* dWk, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (r < 1 || r > 64) return DSA_ERR_RANK;
+  if (dv.BH == 0) return DSA_OK;
+  if (!Q || !K || !Wq || !Wk || !loss || !dWq || !dWk) return DSA_ERR_NULL;
+  const size_t need = predictor_grad_workspace_bytes(dv.BH, shape->H, dv.g.NB, dv.d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return DSA_ERR_WORKSPACE;
+  PGradArgs g;
+  predictor_grad_carve(g, workspace, dv.BH, shape->H, dv.g.NB, dv.d);
+  g.Wq = Wq; g.Wk = Wk; g.loss = loss; g.dWq = dWq; g.dWk = dWk;
+  g.B = shape->B; g.H = shape->H; g.NB = dv.g.NB; g.r = r;
+  // tile means only (no projection): the pooling kernel of the predictor
+  PredictArgs a;
+  a.Q = Q; a.K = K; a.Wq = Wq; a.Wk = Wk;
+  a.Qbar = nullptr; a.Kbar = nullptr; a.S = nullptr;
+  a.Pq = const_cast<float*>(g.Pq); a.Pk = const_cast<float*>(g.Pk);
+  a.g = dv.g; a.B = shape->B; a.H = shape->H; a.r = r;
+  hipError_t e = launch_pool_project(a, dv.io_f32, dv.d, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_predictor_grad(g, dv.io_f32, dv.d, stream));
+}
+
 dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, int32_t kmax, int32_t* idx,
                       hipStream_t stream) {
   Derived dv;

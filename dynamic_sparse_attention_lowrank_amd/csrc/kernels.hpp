@@ -40,8 +40,33 @@ struct PredictArgs {
   float* S;
   Geo g;
   int B, H, r;
+  float* Pq = nullptr;   // optional: tile means of Q, [B*H][NB][d] fp32
+  float* Pk = nullptr;   // optional: tile means of K
 };
 hipError_t launch_predict(const PredictArgs& a, int io_f32, int d, hipStream_t s);
+
+// Stage-one predictor training: loss and weight gradients from the Gram
+// matrices of the pooled Q and K.
+struct PGradArgs {
+  const float* Pq;      // [B*H][NB][d] tile means (pool_project with Pq/Pk set)
+  const float* Pk;
+  float* Gq;            // workspace [B*H][d][d]: Pq^T Pq
+  float* Gk;            // workspace [B*H][d][d]: Pk^T Pk
+  float* M;             // workspace [H][d][d]: Wq Wk^T - I
+  float* qpart;         // workspace [B*H][d][r]: per-(b,h) dWq rows (unscaled)
+  float* kpart;         // workspace [B*H][d/16][d][r]: per row block dWk parts
+  float* lpart;         // workspace [B*H][d/16]: per row block loss parts
+  const void* Wq;       // [H][d][r], I/O dtype
+  const void* Wk;
+  float* loss;          // [B][H]
+  float* dWq;           // [H][d][r] fp32
+  float* dWk;
+  int B, H, NB, r;
+};
+size_t predictor_grad_workspace_bytes(int BH, int H, int NB, int d);
+// points the workspace arrays of `a` (Pq, Pk, Gq, Gk, M, parts) into `workspace`
+void predictor_grad_carve(PGradArgs& a, void* workspace, int BH, int H, int NB, int d);
+hipError_t launch_predictor_grad(const PGradArgs& a, int io_f32, int d, hipStream_t s);
 
 struct SelectArgs {
   const float* S;

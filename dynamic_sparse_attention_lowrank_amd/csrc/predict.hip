@@ -11,7 +11,8 @@
 //
 // Kernel 1 (pool_project): one work-group per (tensor, head, tile); 16-byte
 //   coalesced row loads, fp32 column sums, LDS tree over token groups in a fixed
-//   order, then the d x r projection.
+//   order, then the d x r projection (optionally also stores the tile means, and
+//   with no Qbar/Kbar output only those, for the predictor's training signal).
 // Kernel 2 (scores): one work-group per (head, 64 query tiles, 256 key blocks);
 //   a thread owns one key block, keeps its Kbar row in registers and writes 64
 //   coalesced scores.  Bound by writing S.
@@ -59,11 +60,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(PredictArgs 
 #pragma unroll
   for (int e = 0; e < CE; ++e) red[rsub * D + c * CE + e] = acc[e];
   __syncthreads();
+  float* __restrict__ P = which ? a.Pk : a.Pq;
   if (tid < D) {
     float s = 0.f;
     for (int q = 0; q < RPG; ++q) s += red[q * D + tid];
     xmean[tid] = s / (float)g.T;
+    if (P) P[((size_t)bh * g.NB + tau) * D + tid] = xmean[tid];
   }
+  if (!out) return;                            // tile means only
   __syncthreads();
   if (tid < a.r) {
     float o = 0.f;

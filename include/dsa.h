@@ -126,6 +126,37 @@ DSA_API dsa_status dsa_predict_select(const dsa_shape* shape, int32_t r, const v
                                       float* Qbar, float* Kbar, int32_t* idx, hipStream_t stream);
 
 /*
+ * dsa_predictor_grad_workspace_bytes -- device workspace that dsa_predictor_grad
+ * needs (0 on invalid arguments), in float32 values: tile means 2*B*H*NB*d, Gram
+ * matrices 2*B*H*d*d, M = Wq Wk^T - I H*d*d, and partial sums B*H*d*64,
+ * B*H*(d/16)*d*64 and B*H*(d/16); each of the eight arrays is rounded up to 256
+ * bytes.
+ */
+DSA_API size_t dsa_predictor_grad_workspace_bytes(const dsa_shape* shape);
+
+/*
+ * dsa_predictor_grad -- training signal of the predictor (DSV page, section 4:
+ *   in stage one the predictor is trained alongside the model; the page gives
+ *   no loss, so this library reads it as follows).  The predictor's score
+ *   S[tau,j] (as defined by dsa_predict) estimates the pooled attention logit
+ *     T[b,h,tau,j] = mean over i in tile tau, n in block j of Q[b,h,i,:] . K[b,h,n,:],
+ *   and the loss of (b, h) is
+ *     loss[b,h] = (1/NB^2) sum_{tau,j} (S[b,h,tau,j] - T[b,h,tau,j])^2.
+ *   dWq[h] and dWk[h] are the gradients of sum_b loss[b,h] with respect to Wq[h]
+ *   and Wk[h] (Q and K receive none).
+ *   Q, K: [B,H,N,d] io dtype.  Wq, Wk: [H,d,r] io dtype.  loss: output [B,H]
+ *   float32.  dWq, dWk: outputs [H,d,r] float32 (overwritten, not accumulated).
+ *   Evaluated as loss = trace(M^T A M C)/NB^2 with M = Wq Wk^T - I and A, C the
+ *   d x d Gram matrices of the tile means of Q and K: no NB x NB array is formed.
+ *   All arithmetic is float32.  r must lie in [1, 64] (DSA_ERR_RANK).
+ *   workspace: device memory of at least dsa_predictor_grad_workspace_bytes(shape)
+ *   bytes, 256-byte aligned (DSA_ERR_WORKSPACE).
+ */
+DSA_API dsa_status dsa_predictor_grad(const dsa_shape* shape, int32_t r, const void* Q, const void* K,
+                                      const void* Wq, const void* Wk, float* loss, float* dWq, float* dWk,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
  * this shape (0 on invalid arguments): 2*B*H*NB*d*64 elements of 2 bytes (bf16
  * io) or 4 bytes (fp32 io).  dsa_attn_fwd first rewrites every key block's K

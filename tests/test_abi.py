@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = set(declared_functions())
     assert {"dsa_predict", "dsa_select", "dsa_predict_select", "dsa_attn_fwd", "dsa_attn_bwd",
-            "dsa_attn_bwd_workspace_bytes", "dsa_status_string", "dsa_version"} <= names
+            "dsa_attn_bwd_workspace_bytes", "dsa_status_string", "dsa_version", "dsa_predictor_grad",
+            "dsa_predictor_grad_workspace_bytes"} <= names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -74,6 +75,20 @@ def test_entry_point_validation(L):
     assert ps(ctypes.byref(sh), 16, 17, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == 4
     assert ps(ctypes.byref(sh), 16, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE) == 1
     assert ps(None, 16, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == 1
+    pneed = lib.dsa_predictor_grad_workspace_bytes(ctypes.byref(sh))
+    rnd = lambda x: (x + 255) // 256 * 256
+    BH, NB, d, H, rbs = 2, 16, 64, 2, 64 // 16
+    assert pneed == (2 * rnd(BH * NB * d * 4) + 2 * rnd(BH * d * d * 4) + rnd(H * d * d * 4)   # means, Grams, M
+                     + rnd(BH * d * 64 * 4) + rnd(BH * rbs * d * 64 * 4) + rnd(BH * rbs * 4))  # partial sums
+    pg = lambda shp, r, p, ws, nb: lib.dsa_predictor_grad(shp, r, *p, ws, nb, None)
+    assert pg(ctypes.byref(sh), 0, [FAKE] * 7, FAKE, pneed) == 9
+    assert pg(ctypes.byref(sh), 65, [FAKE] * 7, FAKE, pneed) == 9
+    assert pg(ctypes.byref(sh), 16, [FAKE] * 4 + [None] + [FAKE] * 2, FAKE, pneed) == 1     # no loss output
+    assert pg(ctypes.byref(sh), 16, [FAKE] * 7, None, pneed) == 6
+    assert pg(ctypes.byref(sh), 16, [FAKE] * 7, FAKE, pneed - 1) == 6
+    assert pg(ctypes.byref(sh), 16, [FAKE] * 7, ctypes.c_void_p(0x1010), pneed) == 6
+    assert pg(None, 16, [FAKE] * 7, FAKE, pneed) == 1
+    assert lib.dsa_predictor_grad_workspace_bytes(None) == 0
     fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
     assert fneed == 2 * (1 * 2 * 16 * 64 * 64 * 4)                              # K and V^T: 2*B*H*NB*d*64 fp32
     fw = [FAKE, fneed, None]
@@ -102,6 +117,7 @@ def test_empty_batch_is_a_no_op(L):
     assert L.lib.dsa_predict(ctypes.byref(sh), 16, None, None, None, None, None, None, None, None) == 0
     assert L.lib.dsa_attn_fwd(ctypes.byref(sh), None, None, None, None, None, 4, 0.125, 0, None, None, None, 0,
                               None) == 0
+    assert L.lib.dsa_predictor_grad(ctypes.byref(sh), 16, *([None] * 8), 0, None) == 0
 
 
 def test_workspace_formula(L):
