@@ -215,6 +215,23 @@ def main():
     phase_ms = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
     span_ms = events[0][0].elapsed_time(events[-1][-1]) / args.steps
 
+    # stage-one predictor training signal on the same inputs, timed on its own (not
+    # part of the step above): loss and dWq/dWk, HBM-bound on reading Q and K once
+    pws = torch.empty(dsa.predictor_grad_workspace_bytes(Q, lay), device=dev, dtype=torch.uint8)
+    pout = (torch.empty(B, H, device=dev, dtype=f32), torch.empty(Wq.shape, device=dev, dtype=f32),
+            torch.empty(Wk.shape, device=dev, dtype=f32))
+    for _ in range(2):
+        dsa.predictor_grad(Q, K, Wq, Wk, lay, out=pout, workspace=pws)
+    torch.cuda.synchronize()
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    pe[0].record()
+    for _ in range(10):
+        dsa.predictor_grad(Q, K, Wq, Wk, lay, out=pout, workspace=pws)
+    pe[1].record()
+    torch.cuda.synchronize()
+    pg_ms = pe[0].elapsed_time(pe[1]) / 10
+    pg_bytes = 2.0 * Q.numel() * Q.element_size()
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         a_ = torch.zeros(n, device=dev, dtype=torch.int32)
@@ -265,6 +282,8 @@ def main():
         "event_ms_per_step": round(span_ms, 4),
         "counted_flop": {"fwd": flop_fwd, "bwd": flop_bwd, "pairs": pairs},
         "roofline": roofline,
+        "predictor_grad": {"ms": round(pg_ms, 4), "bound": "hbm", "algorithmic_bytes": pg_bytes,
+                           "GBps": round(pg_bytes / (pg_ms * 1e-3) / 1e9, 1), "peak_GBps": 8000.0},
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:

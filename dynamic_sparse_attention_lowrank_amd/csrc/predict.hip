@@ -26,7 +26,7 @@ namespace {
 constexpr int kPoolThreads = 256;
 
 template <typename T, int D>
-__global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(PredictArgs a) {
+__device__ __forceinline__ void pool_project_body(const PredictArgs& a) {
   constexpr int CE = Elem<T>::kChunkElems;
   constexpr int CPR = D / CE;                  // 16-byte chunks per token row
   constexpr int RPG = kPoolThreads / CPR;      // token rows loaded per pass
@@ -76,6 +76,18 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(PredictArgs 
   }
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(PredictArgs a) {
+  pool_project_body<T, D>(a);
+}
+
+// the same body with tile means only (Qbar = Kbar = null), named apart so that
+// profiles keep the predictor's pooling and the training signal's apart
+template <typename T, int D>
+__global__ __launch_bounds__(kPoolThreads) void tile_mean_kernel(PredictArgs a) {
+  pool_project_body<T, D>(a);
+}
+
 constexpr int kScoreRows = 64;
 constexpr int kScoreCols = 256;
 
@@ -111,7 +123,10 @@ __global__ __launch_bounds__(kScoreCols) void scores_kernel(PredictArgs a) {
 template <typename T, int D>
 hipError_t launch_pool(const PredictArgs& a, hipStream_t s) {
   const int grid = 2 * a.B * a.H * a.g.NB;
-  hipLaunchKernelGGL((pool_project_kernel<T, D>), dim3(grid), dim3(kPoolThreads), 0, s, a);
+  if (a.Qbar)
+    hipLaunchKernelGGL((pool_project_kernel<T, D>), dim3(grid), dim3(kPoolThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((tile_mean_kernel<T, D>), dim3(grid), dim3(kPoolThreads), 0, s, a);
   return hipGetLastError();
 }
 
