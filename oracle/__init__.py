@@ -8,4 +8,5 @@ from .dsa_oracle import (  # noqa: F401
     attn_tile, attn_fwd_head, attn_bwd_tile, attn_bwd_head, attn_bwd_key_block,
     predict, select, attn_fwd, attn_bwd,
     tile_means, pooled_logits, predictor_loss_head, predictor_grad_head, predictor_grad,
+    rope_sections, rope_angles, rope3d,
 )

@@ -30,7 +30,9 @@ its reason in the design notes of this repository):
   scale = 1/sqrt(d), non-causal; LSE is a natural log;
 * backward: the block mask is held fixed (no gradient reaches the predictor);
 * predictor training (stage one, section 4): squared error of the scores against
-  the pooled attention logits, gradient for Wq and Wk only.
+  the pooled attention logits, gradient for Wq and Wk only;
+* 3-D rotary positions (second page): per-axis rotary encoding of Q and K with a
+  global time offset (see ``rope3d``).
 
 Every array here is float64 (inputs are upcast exactly from their storage
 dtype).  Library primitives used as steps: matrix products, argsort/lexsort,
@@ -187,6 +189,50 @@ def predictor_grad(Q, K, Wq, Wk, geom: "Geometry"):
             dWq[h] += gq
             dWk[h] += gk
     return loss, dWq, dWk
+
+
+# ----------------------------------------------------------------------------
+# 3-D rotary positions (second page, section 2: each frame's position in time is
+# the start index of its chunk plus its index inside the chunk -- a global time
+# index; with height and width this is a 3-D positional encoding).  The page
+# gives no formula.  Reading: rotary encoding per axis -- the head dimension is
+# cut into a time, a height and a width section of consecutive pairs (time takes
+# what a three-way split leaves over: 22/21/21 pairs at d = 128); pair i of a
+# section of 2m dimensions is rotated by the angle (position on that axis) *
+# base^(-2i / 2m), base = 10000; positions are the latent coordinates plus an
+# offset per axis (t0: the chunk's global start frame).  Applied to Q and K.
+# ----------------------------------------------------------------------------
+def rope_sections(d: int) -> Tuple[int, int, int]:
+    """Pairs per axis (time, height, width)."""
+    pairs = d // 2
+    py = pairs // 3
+    return pairs - 2 * py, py, py
+
+
+def rope_angles(geom: "Geometry", d: int, base: float = 10000.0, offsets=(0, 0, 0)) -> np.ndarray:
+    """Angle of every (token, pair): [N, d/2], fp64."""
+    n = np.arange(geom.N)
+    pos = (n // (geom.Lh * geom.Lw) + offsets[0], (n // geom.Lw) % geom.Lh + offsets[1], n % geom.Lw + offsets[2])
+    cols = []
+    for axis, m in enumerate(rope_sections(d)):
+        for i in range(m):
+            cols.append(pos[axis] * base ** (-2.0 * i / (2 * m)))
+    return np.stack(cols, axis=1).astype(np.float64)
+
+
+def rope3d(X: np.ndarray, geom: "Geometry", base: float = 10000.0, offsets=(0, 0, 0), inverse: bool = False):
+    """Rotate every pair (X[n, 2p], X[n, 2p+1]) of one head's [N, d] rows by the
+    token's angle for pair p (by minus that angle when ``inverse``)."""
+    X = np.asarray(X, dtype=np.float64)
+    a = rope_angles(geom, X.shape[1], base, offsets)
+    if inverse:
+        a = -a
+    c, s = np.cos(a), np.sin(a)
+    u, v = X[:, 0::2], X[:, 1::2]
+    out = np.empty_like(X)
+    out[:, 0::2] = u * c - v * s
+    out[:, 1::2] = u * s + v * c
+    return out
 
 
 # ----------------------------------------------------------------------------

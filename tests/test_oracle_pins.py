@@ -245,6 +245,69 @@ def test_predictor_grad_sums_over_batch(tiny):
         assert np.abs(gk[h] - parts[0][2] - parts[1][2]).max() <= 1e-15 * np.abs(gk[h]).max()
 
 
+# ---------------------------------------------------------------- 3-D rotary positions
+def test_rope_sections():
+    """R-1: time, height and width sections of pairs; time takes the remainder."""
+    assert oracle.rope_sections(128) == (22, 21, 21)
+    assert oracle.rope_sections(64) == (12, 10, 10)
+    assert oracle.rope_sections(6) == (1, 1, 1)
+
+
+def test_rope_hand_cases():
+    """R-2: with one pair per axis every frequency is 1, so token (t, y, x) turns
+    (1, 0) into (cos p, sin p) and (0, 1) into (-sin p, cos p) for p = t, y, x; with
+    two pairs per axis the second pair of a section turns by p * base^(-1/2)."""
+    geom = Geometry(2, 3, 4, 1, 1, 1)
+    n = (1 * 3 + 2) * 4 + 3                                       # (t, y, x) = (1, 2, 3)
+    X = np.zeros((geom.N, 6))
+    X[n] = [1, 0, 1, 0, 0, 1]
+    Y = oracle.rope3d(X, geom)
+    want = [math.cos(1), math.sin(1), math.cos(2), math.sin(2), -math.sin(3), math.cos(3)]
+    assert np.abs(Y[n] - want).max() < 1e-15
+    X2 = np.zeros((geom.N, 12))
+    X2[n, 2] = 1.0                                                 # second time pair, x-component
+    Y2 = oracle.rope3d(X2, geom, base=10000.0)
+    assert abs(Y2[n, 2] - math.cos(0.01)) < 1e-15 and abs(Y2[n, 3] - math.sin(0.01)) < 1e-15
+    Y3 = oracle.rope3d(X, geom, offsets=(4, 0, -3))                # offsets move the positions
+    want3 = [math.cos(5), math.sin(5), math.cos(2), math.sin(2), -math.sin(0), math.cos(0)]
+    assert np.abs(Y3[n] - want3).max() < 1e-15
+
+
+def test_rope_relative_position_and_inverse():
+    """R-3: rotations keep each pair's length, undo with the inverse, and q.k after
+    rotation depends only on the difference of positions: shifting every position
+    by the same offset leaves all dot products unchanged."""
+    geom = Geometry(3, 4, 4, 1, 2, 2)
+    rng = np.random.default_rng(2)
+    Q = rng.standard_normal((geom.N, 16))
+    K = rng.standard_normal((geom.N, 16))
+    Qr, Kr = oracle.rope3d(Q, geom), oracle.rope3d(K, geom)
+    assert np.abs((Qr[:, 0::2] ** 2 + Qr[:, 1::2] ** 2) - (Q[:, 0::2] ** 2 + Q[:, 1::2] ** 2)).max() < 1e-12
+    assert np.abs(oracle.rope3d(Qr, geom, inverse=True) - Q).max() < 1e-12
+    off = (7, -2, 5)
+    G0 = Qr @ Kr.T
+    G1 = oracle.rope3d(Q, geom, offsets=off) @ oracle.rope3d(K, geom, offsets=off).T
+    assert np.abs(G0 - G1).max() < 1e-11 * np.abs(G0).max()
+    # and it does change with a position difference (a shift of K alone)
+    G2 = Qr @ oracle.rope3d(K, geom, offsets=(1, 0, 0)).T
+    assert np.abs(G0 - G2).max() > 1e-3
+
+
+def test_rope_global_time_index():
+    """R-4: a chunk of frames s..s+c-1 rotated with time offset s equals those
+    frames' rows of the whole clip rotated from 0 (position = chunk start + index)."""
+    whole = Geometry(6, 4, 8, 1, 2, 2)
+    chunk = Geometry(2, 4, 8, 1, 2, 2)
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((whole.N, 12))
+    per_frame = whole.Lh * whole.Lw
+    Yw = oracle.rope3d(X, whole)
+    for s0 in (0, 2, 4):
+        rows = slice(s0 * per_frame, (s0 + 2) * per_frame)
+        Yc = oracle.rope3d(X[rows], chunk, offsets=(s0, 0, 0))
+        assert np.abs(Yc - Yw[rows]).max() < 1e-13
+
+
 # ---------------------------------------------------------------- selection
 def brute_force_select(scores, tau, k):
     """Max-sum subset of k-1 other blocks; equal sums -> lexicographically smallest."""
