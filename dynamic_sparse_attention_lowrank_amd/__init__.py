@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
     "bwd_workspace_bytes", "fwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
-    "predict_select", "predictor_grad", "predictor_grad_workspace_bytes",
+    "predict_select", "predictor_grad", "predictor_grad_workspace_bytes", "rope3d",
 ]
 
 F32 = 0
@@ -67,6 +67,8 @@ def _load():
     L.dsa_predictor_grad_workspace_bytes.argtypes = [sp]
     L.dsa_predictor_grad.restype = ctypes.c_int
     L.dsa_predictor_grad.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_rope3d.restype = ctypes.c_int
+    L.dsa_rope3d.argtypes = [sp, i32, f32, i32, i32, i32, i32, vp, vp, vp]
     L.dsa_attn_fwd.restype = ctypes.c_int
     L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
     L.dsa_attn_fwd_workspace_bytes.restype = sz
@@ -203,6 +205,20 @@ def predict_select(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch
     _check(_L().dsa_predict_select(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(k), kmax,
                                    _ptr(Qbar), _ptr(Kbar), _ptr(idx), _stream()))
     return Qbar, Kbar, idx
+
+
+def rope3d(X: torch.Tensor, layout: Layout, base: float = 10000.0, offsets: Tuple[int, int, int] = (0, 0, 0),
+           inverse: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """3-D rotary positions of X [B,H,N,d] (bf16 or fp32); `out` may be X (in place)."""
+    _dev(X)
+    sh = _shape(X, layout)
+    Y = torch.empty_like(X) if out is None else out
+    if Y.shape != X.shape or Y.dtype != X.dtype or not Y.is_contiguous():
+        raise ValueError("rope3d: out must be a contiguous tensor of X's shape and dtype")
+    dt = F32 if X.dtype == torch.float32 else BF16
+    _check(_L().dsa_rope3d(ctypes.byref(sh), dt, float(base), int(offsets[0]), int(offsets[1]), int(offsets[2]),
+                           int(bool(inverse)), _ptr(X), _ptr(Y), _stream()))
+    return Y
 
 
 def predictor_grad_workspace_bytes(Q: torch.Tensor, layout: Layout) -> int:

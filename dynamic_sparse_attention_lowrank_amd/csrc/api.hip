@@ -7,6 +7,8 @@
 #include "dsa.h"
 #include "kernels.hpp"
 
+#include <cmath>
+
 using namespace dsa;
 
 namespace {
@@ -160,6 +162,28 @@ dsa_status dsa_predictor_grad(const dsa_shape* shape, int32_t r, const void* Q, 
   hipError_t e = launch_pool_project(a, dv.io_f32, dv.d, stream);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_predictor_grad(g, dv.io_f32, dv.d, stream));
+}
+
+dsa_status dsa_rope3d(const dsa_shape* shape, int32_t dtype, float base, int32_t t0, int32_t y0, int32_t x0,
+                      int32_t inverse, const void* X, void* Y, hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (!(base > 1.f) || !(base < 3.0e38f)) return DSA_ERR_SHAPE;       // also rejects NaN
+  const int32_t lim = 1 << 30;
+  if (t0 < -lim || t0 > lim || y0 < -lim || y0 > lim || x0 < -lim || x0 > lim) return DSA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return DSA_ERR_SHAPE;
+  if (dv.BH == 0) return DSA_OK;
+  if (!X || !Y) return DSA_ERR_NULL;
+  const uintptr_t pair_bytes = dtype == DSA_F32 ? 8 : 4;
+  if (((uintptr_t)X | (uintptr_t)Y) & (pair_bytes - 1)) return DSA_ERR_SHAPE;
+  RopeArgs a;
+  a.X = X; a.Y = Y; a.g = dv.g; a.BH = dv.BH; a.d = dv.d;
+  a.t0 = t0; a.y0 = y0; a.x0 = x0;
+  a.log2_base = std::log2(base);
+  a.inverse = inverse;
+  return hip_status(launch_rope3d(a, dtype == DSA_F32, stream));
 }
 
 dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, int32_t kmax, int32_t* idx,

@@ -68,6 +68,18 @@ size_t predictor_grad_workspace_bytes(int BH, int H, int NB, int d);
 void predictor_grad_carve(PGradArgs& a, void* workspace, int BH, int H, int NB, int d);
 hipError_t launch_predictor_grad(const PGradArgs& a, int io_f32, int d, hipStream_t s);
 
+// 3-D rotary positions of one [B*H][N][d] tensor (X -> Y, Y may be X).
+struct RopeArgs {
+  const void* X;
+  void* Y;
+  Geo g;
+  int BH, d;
+  int t0, y0, x0;       // position offsets per axis
+  float log2_base;
+  int inverse;          // 1: rotate by minus the angle
+};
+hipError_t launch_rope3d(const RopeArgs& a, int f32, hipStream_t s);
+
 struct SelectArgs {
   const float* S;
   const int32_t* kvec;

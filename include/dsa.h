@@ -157,6 +157,30 @@ DSA_API dsa_status dsa_predictor_grad(const dsa_shape* shape, int32_t r, const v
                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dsa_rope3d -- 3-D rotary positions (second page, gist.science/ar/paper/2603.06664,
+ *   section 2: a frame's time position is its chunk's start index plus its index in
+ *   the chunk, a global time index; the page gives no formula, so this library
+ *   reads it as rotary encoding per axis).
+ *   The d/2 adjacent pairs (X[n,2p], X[n,2p+1]) of every token row are cut into a
+ *   time, a height and a width section of mt, mh, mw pairs (mh = mw = (d/2)/3,
+ *   mt = d/2 - 2*mh: 22/21/21 at d = 128, 12/10/10 at d = 64).  Pair i of a section
+ *   of m pairs is rotated by
+ *     angle = (c + c0) * base^(-i/m),   c = the token's latent coordinate on that
+ *     axis (t, y or x), c0 = t0, y0 or x0,
+ *   that is Y = (u cos a - v sin a, u sin a + v cos a) for (u, v) = the pair;
+ *   inverse = 1 rotates by -angle (maps gradients of rotated tensors back).
+ *   X, Y: [B,H,N,d] arrays of element type `dtype` (DSA_BF16 or DSA_F32, any io);
+ *   Y may equal X (in place).  Arithmetic is fp32 (sincosf), one rounding to the
+ *   output type (round to nearest even for bf16).  Apply it to Q and K before
+ *   dsa_predict / dsa_predict_select / dsa_attn_fwd, and with inverse = 1 to the
+ *   dQ and dK of dsa_attn_bwd.
+ *   Errors: base must be finite and > 1, |t0|, |y0|, |x0| <= 2^30, inverse 0 or 1,
+ *   X and Y aligned to one pair (4 bytes bf16, 8 bytes fp32): DSA_ERR_SHAPE.
+ */
+DSA_API dsa_status dsa_rope3d(const dsa_shape* shape, int32_t dtype, float base, int32_t t0, int32_t y0, int32_t x0,
+                              int32_t inverse, const void* X, void* Y, hipStream_t stream);
+
+/*
  * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
  * this shape (0 on invalid arguments): 2*B*H*NB*d*64 elements of 2 bytes (bf16
  * io) or 4 bytes (fp32 io).  dsa_attn_fwd first rewrites every key block's K

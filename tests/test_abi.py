@@ -30,7 +30,7 @@ def test_header_declares_entry_points():
     names = set(declared_functions())
     assert {"dsa_predict", "dsa_select", "dsa_predict_select", "dsa_attn_fwd", "dsa_attn_bwd",
             "dsa_attn_bwd_workspace_bytes", "dsa_status_string", "dsa_version", "dsa_predictor_grad",
-            "dsa_predictor_grad_workspace_bytes"} <= names
+            "dsa_predictor_grad_workspace_bytes", "dsa_rope3d"} <= names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -89,6 +89,15 @@ def test_entry_point_validation(L):
     assert pg(ctypes.byref(sh), 16, [FAKE] * 7, ctypes.c_void_p(0x1010), pneed) == 6
     assert pg(None, 16, [FAKE] * 7, FAKE, pneed) == 1
     assert lib.dsa_predictor_grad_workspace_bytes(None) == 0
+    rp = lambda shp, dt, base, offs, inv, x, y: lib.dsa_rope3d(shp, dt, base, *offs, inv, x, y, None)
+    assert rp(ctypes.byref(sh), 7, 1e4, (0, 0, 0), 0, FAKE, FAKE) == 5
+    assert rp(ctypes.byref(sh), 1, 1.0, (0, 0, 0), 0, FAKE, FAKE) == 2                  # base must exceed 1
+    assert rp(ctypes.byref(sh), 1, float("nan"), (0, 0, 0), 0, FAKE, FAKE) == 2
+    assert rp(ctypes.byref(sh), 1, 1e4, (0, 0, 0), 2, FAKE, FAKE) == 2                  # inverse is 0 or 1
+    assert rp(ctypes.byref(sh), 1, 1e4, (2 ** 30 + 1, 0, 0), 0, FAKE, FAKE) == 2
+    assert rp(ctypes.byref(sh), 1, 1e4, (0, 0, 0), 0, None, FAKE) == 1
+    assert rp(ctypes.byref(sh), 0, 1e4, (0, 0, 0), 0, ctypes.c_void_p(0x1004), FAKE) == 2   # fp32 pairs: 8-byte aligned
+    assert rp(None, 1, 1e4, (0, 0, 0), 0, FAKE, FAKE) == 1
     fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
     assert fneed == 2 * (1 * 2 * 16 * 64 * 64 * 4)                              # K and V^T: 2*B*H*NB*d*64 fp32
     fw = [FAKE, fneed, None]
@@ -118,6 +127,7 @@ def test_empty_batch_is_a_no_op(L):
     assert L.lib.dsa_attn_fwd(ctypes.byref(sh), None, None, None, None, None, 4, 0.125, 0, None, None, None, 0,
                               None) == 0
     assert L.lib.dsa_predictor_grad(ctypes.byref(sh), 16, *([None] * 8), 0, None) == 0
+    assert L.lib.dsa_rope3d(ctypes.byref(sh), 1, 1e4, 0, 0, 0, 0, None, None, None) == 0
 
 
 def test_workspace_formula(L):
