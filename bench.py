@@ -232,6 +232,26 @@ def main():
     pg_ms = pe[0].elapsed_time(pe[1]) / 10
     pg_bytes = 2.0 * Q.numel() * Q.element_size()
 
+    # 3-D rotary positions of Q and K (forward) and of dQ and dK (inverse), timed on
+    # their own: four HBM passes of read + write
+    rq, rk = torch.empty_like(Q), torch.empty_like(K)
+    for _ in range(2):
+        dsa.rope3d(Q, lay, out=rq)
+    torch.cuda.synchronize()
+    re_ = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    re_[0].record()
+    for _ in range(10):
+        dsa.rope3d(Q, lay, out=rq)
+        dsa.rope3d(K, lay, out=rk)
+        dsa.rope3d(dQ, lay, inverse=True, out=dQ)
+        dsa.rope3d(dK, lay, inverse=True, out=dK)
+    re_[1].record()
+    torch.cuda.synchronize()
+    rope_ms = re_[0].elapsed_time(re_[1]) / 10
+    rope_bytes = 2.0 * (Q.numel() * Q.element_size() + K.numel() * K.element_size() +
+                        dQ.numel() * dQ.element_size() + dK.numel() * dK.element_size())
+    del rq, rk
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         a_ = torch.zeros(n, device=dev, dtype=torch.int32)
@@ -282,6 +302,9 @@ def main():
         "event_ms_per_step": round(span_ms, 4),
         "counted_flop": {"fwd": flop_fwd, "bwd": flop_bwd, "pairs": pairs},
         "roofline": roofline,
+        "rope3d": {"ms": round(rope_ms, 4), "what": "Q, K rotated + dQ, dK rotated back", "bound": "hbm",
+                   "algorithmic_bytes": rope_bytes, "GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
+                   "peak_GBps": 8000.0},
         "predictor_grad": {"ms": round(pg_ms, 4), "bound": "hbm", "algorithmic_bytes": pg_bytes,
                            "GBps": round(pg_bytes / (pg_ms * 1e-3) / 1e9, 1), "peak_GBps": 8000.0},
         "source_hash": source_hash(),
