@@ -1,9 +1,9 @@
 // LDS tiles of 64 tokens x D elements for the attention kernels (gfx950).
 //
 // Layout: row-major [64][D]; a token row is D*sizeof(T) bytes = CPR 16-byte
-// chunks, and chunk c of row r sits at slot c ^ row_swz(r) (a bijection of
-// r mod min(CPR,16)), so both the row-wise operand reads and the transposing
-// reads of 4-row groups are free of bank conflicts at d = 128.
+// chunks, and chunk c of row r sits at slot c ^ row_swz(r), so both the row-wise
+// operand reads and the transposing reads of 4-row groups are free of bank
+// conflicts (see row_swz).
 //
 // Tiles are filled either by direct global->LDS loads (dma_*: the backward) or
 // through registers (row_*: the forward's Q tile, 128 threads).  Global accesses
@@ -28,13 +28,23 @@ struct TileCfg {
   static constexpr int kRowChunks = 64 * kCPR;                // LDS chunks of a row-major tile
 };
 
-// Row swizzle: a bijection of r mod RSw whose bits 1-2 are r mod 4 (bit 0: bit 2 of
-// r, bit 3: bit 3 of r).  16 consecutive rows reading one chunk column hit 16
-// distinct slots, and 4 consecutive rows (starting at a multiple of 4) reading a
-// 32-byte column pair hit 8 distinct slots -- both conflict-free at d = 128.
+// Row swizzle h(r), periodic in 16 rows.  Measured on gfx950: a 16-byte-per-lane
+// read is served 16 lanes at a time and is conflict-free when those lanes hit 16
+// distinct 16-byte slots of a 256-byte window; the transposing 8-byte read
+// (ds_read_b64_tr_b16) is served 32 lanes -- two 4-row groups, i.e. 8 consecutive
+// rows -- at a time and needs their 32-byte column segments to be 8 distinct
+// segments of the window.  So h must be a bijection on 16 consecutive rows (row
+// reads of one chunk column) and h >> 1 a bijection on each aligned block of 8
+// rows (transposing reads of one 32-byte segment):
+//   d = 128 (16 slots per 256-byte row):  h = ((r & 7) << 1) | (r >> 3 & 1)
+//   d = 64  (8 slots per 128-byte row, two rows per window): h = (r >> 1 & 3) << 1 |
+//     (r >> 3 & 1), a bijection on each parity class of 16 rows and, with h >> 1,
+//     on each parity class of an 8-row block.
 template <typename T, int D>
 __device__ __forceinline__ int row_swz(int r) {
-  return (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8)) & (TileCfg<T, D>::kRSw - 1);
+  if constexpr (TileCfg<T, D>::kRSw == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else if constexpr (TileCfg<T, D>::kRSw == 8) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  else return r & (TileCfg<T, D>::kRSw - 1);
 }
 template <typename T, int D>
 __device__ __forceinline__ int row_slot(int r, int c) {
