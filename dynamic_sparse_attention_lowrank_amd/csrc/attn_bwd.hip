@@ -213,7 +213,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ float st0[2][64], st1[2][64];    // [LSE, D][query row]
 
   const Geo g = a.g;
-  const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
+  const int L = blockIdx.x;                 // natural order (see common.hpp)
   const int bh = L / g.NB;
   const int j = L - bh * g.NB;
   const int tid = threadIdx.x;
@@ -440,7 +440,7 @@ void bwd_dq_kernel(BwdArgs a) {
   __shared__ u32x4 v0[C::kRowChunks], v1[C::kRowChunks];
 
   const Geo g = a.g;
-  const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
+  const int L = blockIdx.x;                 // natural order (see common.hpp)
   const int bh = L / g.NB;
   const int tau = L - bh * g.NB;
   const int tid = threadIdx.x;

@@ -290,7 +290,7 @@ void attn_fwd_kernel(FwdArgs a) {
   float (*mrg_ml)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + 2 * C::kDTiles * 16 * 64 * 4);
 
   const Geo g = a.g;
-  const int L = xcd_remap(blockIdx.x, a.BH * g.NB);
+  const int L = blockIdx.x;                 // natural order (see common.hpp)
   const int bh = L / g.NB;
   const int tau = L - bh * g.NB;
   const int tid = threadIdx.x;
