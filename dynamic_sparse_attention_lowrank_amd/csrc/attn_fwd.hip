@@ -108,6 +108,86 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(FwdArgs a) {
   }
 }
 
+// Same output for 16-bit inputs, through LDS: the block's K and V rows are staged
+// with coalesced 16-byte loads (256 threads, every row read as one 256-byte run)
+// into XOR-swizzled row-major tiles; each K output chunk is then one 16-byte LDS
+// read, and each V^T output chunk (8 keys of one d) two transposing LDS reads of
+// 4 keys -- with the perm16 key order the 8 keys of a chunk are two runs of 4
+// consecutive keys -- converted to fp16.  Every global store is coalesced.
+template <int D>
+__global__ __launch_bounds__(256) void kv_prep16_kernel(FwdArgs a) {
+  typedef bf16 T;
+  typedef f16 PT;
+  using C = TileCfg<T, D>;
+  constexpr int CE = C::kCE;                                   // 8 elements per chunk
+  constexpr int CPR = C::kCPR;
+  constexpr int FC = Elem<T>::kFragChunks;
+  constexpr int KF = D / 16 * FC;                              // K chunks per lane per half
+  constexpr int NCH = 64 * CPR;                                // chunks of a 64-row tile
+  static_assert(CE == 8 && Elem<PT>::kFragChunks == 1, "16-bit elements");
+  __shared__ u32x4 kt[NCH], vt[NCH];
+  const Geo g = a.g;
+  const int bj = blockIdx.x;
+  const int bh = bj / g.NB, j = bj - bh * g.NB;
+  const size_t hoff = (size_t)bh * g.N * D;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(a.K) + hoff;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + hoff;
+  const int base = tile_base(g, j);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NCH / 256; ++i) {
+    const int idx = tid + 256 * i, r = idx / CPR, c = idx % CPR;
+    u32x4 kv = u32x4{0, 0, 0, 0}, vv = kv;
+    if (r < g.T) {
+      const size_t off = (size_t)(base + member_offset(g, r)) * D + c * CE;
+      kv = *reinterpret_cast<const u32x4*>(Kh + off);
+      vv = *reinterpret_cast<const u32x4*>(Vh + off);
+    }
+    kt[row_slot<T, D>(r, c)] = kv;
+    vt[row_slot<T, D>(r, c)] = vv;
+  }
+  __syncthreads();
+  u32x4* __restrict__ ko = reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.Kf) + (size_t)bj * 64 * D);
+  u32x4* __restrict__ vo = reinterpret_cast<u32x4*>(reinterpret_cast<PT*>(a.Vt) + (size_t)bj * 64 * D);
+  // K: output chunk (w, f, lane) = chunk d0/CE of key row 32w + lane%32
+#pragma unroll
+  for (int i = 0; i < 2 * KF * 64 / 256; ++i) {
+    const int it = tid + 256 * i;
+    const int lane = it % 64, f = (it / 64) % KF, w = it / (64 * KF);
+    const int r = 32 * w + (lane & 31);
+    const int d0 = 16 * (f / FC) + 8 * (lane >> 5) + CE * (f % FC);
+    ko[it] = kt[row_slot<T, D>(r, d0 / CE)];
+  }
+  // V^T: output chunk (w, f = 2t + s, lane) = V[key(p0 + e)][32t + lane%32], e < 8,
+  // p0 = 32w + 16s + 8(lane/32); lanes 16g..16g+15 read columns 32t + 16(g%2) + i
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const char* vb = reinterpret_cast<const char*>(vt);
+#pragma unroll
+  for (int i = 0; i < NCH / 256; ++i) {
+    const int o = tid + 256 * i;
+    const int lane = o % 64, wf = o / 64;
+    const int w = wf / (D / 16), f = wf % (D / 16);
+    const int t = f >> 1, s2 = f & 1, hh = lane >> 5, li = lane & 15;
+    const int p0 = 32 * w + 16 * s2 + 8 * hh;                  // multiple of 8
+    const int keyA = 16 * (p0 >> 4) + perm16(p0 & 15);         // positions p0..p0+3
+    const int keyB = 16 * (p0 >> 4) + perm16((p0 & 15) + 4);   // positions p0+4..p0+7
+    const int col = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+    const int chunk = col >> 3, byte = (col & 7) * 2;
+    const int ra = keyA + (li >> 2), rb = keyB + (li >> 2);
+    const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (bf16x4 __attribute__((address_space(3)))*)(vb + row_slot<T, D>(ra, chunk) * 16 + byte));
+    const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (bf16x4 __attribute__((address_space(3)))*)(vb + row_slot<T, D>(rb, chunk) * 16 + byte));
+    PT e[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      e[q] = (PT)(float)x0[q];
+      e[4 + q] = (PT)(float)x1[q];
+    }
+    vo[o] = *reinterpret_cast<const u32x4*>(e);
+  }
+}
+
 // ------------------------------------------------------------ 2. attention
 template <typename T, int D>
 struct FwdCfg {
@@ -410,7 +490,10 @@ hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
   FwdArgs a = a0;
   a.Kf = a0.Vt;
   a.Vt = reinterpret_cast<char*>(a0.Vt) + (size_t)a0.BH * a0.g.NB * 64 * D * sizeof(T);
-  hipLaunchKernelGGL((kv_prep_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((kv_prep16_kernel<D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((kv_prep_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
   if (a.g.T == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
   else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
   return hipGetLastError();
