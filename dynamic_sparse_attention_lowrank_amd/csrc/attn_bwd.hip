@@ -8,14 +8,16 @@
 //
 // Precision: P and dS are computed in fp32 inside the kernels.  dV = P^T dO runs
 // on fp16 matrix cores (P in [0,1] rounded to fp16, dO from an fp16 copy written
-// by the prepare phase -- exact for |dO| < 65504); the products with dS (dK, dQ)
+// by the prepare phase and scaled by a power of two per (b, h), so that it is
+// exact whatever the size of the gradients); the products with dS (dK, dQ)
 // take it as a bf16 pair hi + lo (see common.hpp) issued twice, so they keep
 // fp32-level accuracy whatever the scale of dS.  D is taken from O as passed in
 // (fp32 O keeps D accurate; with bf16 O its rounding enters D coherently across a
 // whole row).
 //
 // No floating-point atomics, so results are bit-reproducible:
-//   1. prep:     D (fp32) for every token;
+//   1. prep:     the per-(b, h) scale of the fp16 dO copy, then D (fp32) for
+//                every token and the scaled copy;
 //   2. reverse index of the block mask: a bitmap row per key block (bit tau set
 //      if tile tau kept it; integer OR is order-free), popcounts, a per-head
 //      exclusive scan, and an ascending compaction into CSC lists;
@@ -34,7 +36,52 @@ namespace dsa {
 
 namespace {
 
-// ---------------------------------------------------------------- 1. D = rowsum(dO * O)
+// ---------------------------------------------------------------- 1. scale of the fp16 dO copy
+// fp16 keeps 11 significant bits but only 5 exponent bits: a plain conversion
+// drops bits of every bf16 gradient below 2^-17 in magnitude and turns those
+// below 2^-25 into zero, the usual size of training gradients.  The copy holds
+// dO * 2^s instead, one power of two per (b, h), chosen so that the head's
+// largest |dO| lands in [2^14, 2^15): every element within a factor 2^31 of it
+// converts exactly, and the products are brought back by 2^-s in fp32, exactly.
+// (a) per-chunk maxima of the magnitude bits: for finite bf16 values the integer
+//     order of (bits & 0x7fff) is the order of |x|, and a maximum is order-free.
+__global__ __launch_bounds__(256) void do_absmax_kernel(BwdArgs a, int D) {
+  const int bh = blockIdx.x / kDoChunks, c = blockIdx.x - bh * kDoChunks;
+  const size_t n16 = (size_t)a.g.N * D / 8;   // 16-byte chunks (8 bf16) per head
+  const u32x4* __restrict__ p = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(a.dO) + (size_t)bh * a.g.N * D);
+  uint32_t m = 0;
+  for (size_t i = (size_t)c * 256 + threadIdx.x; i < n16; i += (size_t)kDoChunks * 256) {
+    const u32x4 v = p[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, max(v[e] & 0x7fffu, (v[e] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
+  __shared__ uint32_t wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) a.dmax[blockIdx.x] = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+}
+// (b) one wave per (b, h): s = 14 - floor(log2 max|dO|), clamped to [-64, 64]
+//     (2^s and 2^-s stay normal floats); s = 0 for an all-zero or non-finite dO.
+static_assert(kDoChunks == 64, "one lane per chunk");
+__global__ __launch_bounds__(64) void do_scale_kernel(BwdArgs a) {
+  const int bh = blockIdx.x;
+  uint32_t m = a.dmax[(size_t)bh * kDoChunks + threadIdx.x];
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
+  if (threadIdx.x == 0) {
+    int s = 0;
+    if (m != 0u && m < 0x7f80u) {
+      const int e = (int)(m >> 7);            // biased exponent (0: subnormal, below 2^-126)
+      s = e == 0 ? 64 : 14 - (e - 127);
+      s = s < -64 ? -64 : (s > 64 ? 64 : s);
+    }
+    a.dscale[bh] = make_float2(__uint_as_float((uint32_t)(127 + s) << 23), __uint_as_float((uint32_t)(127 - s) << 23));
+  }
+}
+
+// ---------------------------------------------------------------- 2. D = rowsum(dO * O)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   constexpr int CE = Elem<T>::kChunkElems;
@@ -62,10 +109,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < CE; ++e) s = fmaf(ov[e], to_f32(gv[e]), s);
-    if constexpr (sizeof(T) == 2) {            // fp16 copy of dO for the fp16 products of the backward
+    if constexpr (sizeof(T) == 2) {            // scaled fp16 copy of dO for the fp16 products
+      const float up = a.dscale[tok / a.g.N].x;
       f16x8 h;
 #pragma unroll
-      for (int e = 0; e < CE; ++e) h[e] = (f16)to_f32(gv[e]);
+      for (int e = 0; e < CE; ++e) h[e] = (f16)(to_f32(gv[e]) * up);
       *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.dO16) + tok * D + c * CE) = h;
     }
   }
@@ -74,7 +122,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   if (tok < total && c == 0) a.Dvec[tok] = s;
 }
 
-// ---------------------------------------------------------------- 2. reverse index
+// ---------------------------------------------------------------- 3. reverse index
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -168,10 +216,11 @@ __global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- 3. dK, dV
+// ---------------------------------------------------------------- 4. dK, dV
 // Operand types: with bf16 inputs the products that take P or dO (dP = dO V^T,
-// dV = P^T dO) run on fp16 matrix cores (dO from the fp16 copy written by the
-// prepare phase, V converted when loaded, P in [0,1] rounded to fp16); S = Q K^T
+// dV = P^T dO) run on fp16 matrix cores (dO * 2^s from the fp16 copy written by
+// the prepare phase, V converted when loaded, P in [0,1] rounded to fp16; both
+// products are multiplied by 2^-s in fp32, exactly); S = Q K^T
 // and dK = dS^T Q stay bf16, dS as a hi+lo pair.  fp32 inputs use fp32 throughout.
 template <typename T> struct GradType;
 template <> struct GradType<bf16> { typedef f16 type; };
@@ -253,6 +302,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dv[t] = f32x4{};
   }
   const float c2 = a.c;
+  float dinv = 1.f;                           // 2^-s of the fp16 dO copy
+  if constexpr (sizeof(T) == 2) dinv = a.dscale[bh].y;
   const int* list = a.entries + (size_t)bh * g.NB * a.kmax;
   const int* off = a.offsets + (size_t)bh * (g.NB + 1);
   const int e0 = off[j], n = off[j + 1] - e0;
@@ -337,7 +388,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
           float p = fast_exp2(fmaf(sacc[mt][i], c2, -l4[i] * kLog2e));
           if constexpr (!FULL) p = (r0 + i < g.T) ? p : 0.f;      // padding query rows
           pv[4 * hf + i] = p;
-          sv[4 * hf + i] = p * (pacc[mt][i] - d4[i]);
+          sv[4 * hf + i] = p * fmaf(pacc[mt][i], dinv, -d4[i]);
         }
       }
       pf[ks] = to_frag(pv, (G*)nullptr);
@@ -410,13 +461,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         store1(a.dK, orow + 16 * t + l16, a.out_f32, a.scale * dk[t][i]);
-        store1(a.dV, orow + 16 * t + l16, a.out_f32, dv[t][i]);
+        store1(a.dV, orow + 16 * t + l16, a.out_f32, dv[t][i] * dinv);
       }
     }
   }
 }
 
-// ---------------------------------------------------------------- 4. dQ
+// ---------------------------------------------------------------- 5. dQ
 // One work-group of 4 waves per query tile, two waves per SIMD; wave w owns
 // queries 16w..16w+15, whose Q and dO rows stay in registers as the B operands of
 // the 16x16x32 products S^T = K Q^T and dP^T = V dO^T (all bf16).  The kept
@@ -627,6 +678,10 @@ hipError_t launch_prepare_t(const BwdArgs& a, hipStream_t s) {
   constexpr int CPR = D / Elem<T>::kChunkElems;
   const size_t tokens = (size_t)a.BH * a.g.N;
   const int tpb = 256 / CPR;
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL(do_absmax_kernel, dim3((unsigned)(a.BH * kDoChunks)), dim3(256), 0, s, a, D);
+    hipLaunchKernelGGL(do_scale_kernel, dim3((unsigned)a.BH), dim3(64), 0, s, a);
+  }
   hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((tokens + tpb - 1) / tpb)), dim3(256), 0, s, a);
   const size_t nwords = (size_t)a.BH * a.g.NB * a.words;
   const unsigned zgrid = (unsigned)((nwords + 255) / 256 < 65536 ? (nwords + 255) / 256 : 65536);

@@ -104,6 +104,9 @@ hipError_t launch_fused_select(const FusedSelectArgs& a, hipStream_t s);
 // pooled features only (the first half of launch_predict)
 hipError_t launch_pool_project(const PredictArgs& a, int io_f32, int d, hipStream_t s);
 
+// per-(b, h) chunks of the dO magnitude reduction (one wave reduces them)
+constexpr int kDoChunks = 64;
+
 struct BwdArgs {
   const void* Q;
   const void* K;
@@ -123,7 +126,9 @@ struct BwdArgs {
   void* dV;
   // workspace views
   float* Dvec;          // [BH, N]
-  void* dO16;           // [BH, N, d] fp16 copy of dO (bf16 inputs; written by prepare)
+  void* dO16;           // [BH, N, d] fp16 copy of dO * 2^s_bh (bf16 inputs; written by prepare)
+  uint32_t* dmax;       // [BH, kDoChunks] partial max |dO| (bf16 magnitude bits; bf16 inputs)
+  float2* dscale;       // [BH] (2^s_bh, 2^-s_bh): the fp16 copy's exact power-of-two scale
   uint32_t* bitmap;     // [BH, NB, words]   bit tau of row j: tile tau kept block j
   int32_t* counts;      // [BH, NB]
   int32_t* offsets;     // [BH, NB + 1]

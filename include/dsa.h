@@ -201,9 +201,10 @@ DSA_API size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape);
  *   workspace: device memory of at least dsa_attn_fwd_workspace_bytes(shape)
  *   bytes, 256-byte aligned; contents on entry do not matter (DSA_ERR_WORKSPACE).
  *   Softmax statistics and accumulation are float32.  With bf16 io the P.V
- *   product runs on fp16 matrix cores: V is converted to fp16 (exact for
- *   |v| < 65504, the fp16 range; larger magnitudes overflow) and the
- *   probabilities are rounded to fp16.
+ *   product runs on fp16 matrix cores: V is converted to fp16 (a precondition:
+ *   exact for 2^-17 <= |v| < 65504; larger magnitudes overflow, smaller ones are
+ *   rounded to multiples of 2^-24, an absolute error of at most 2^-25 per
+ *   element) and the probabilities are rounded to fp16.
  *   Device-side robustness: k is clamped to [1, kmax]; idx entries outside
  *   [0, NB) are skipped; a row with no valid block gets O = 0, LSE = -inf.
  *   Duplicate entries are the caller's responsibility (dsa_select never makes them).
@@ -217,7 +218,8 @@ DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const voi
  * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for
  * this shape and kmax (0 on invalid arguments).  It holds D = rowsum(dO * O),
  * the reverse (key block -> query tiles) index of idx and, for bf16 inputs, an
- * fp16 copy of dO (B*H*N*d*2 bytes) for the fp16 products of the backward.
+ * fp16 copy of dO (B*H*N*d*2 bytes) for the fp16 products of the backward with
+ * its per-(b, h) scale (B*H*64 partial maxima and B*H float pairs).
  */
 DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
 
@@ -234,9 +236,12 @@ DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax
  *   dQ, dK, dV: outputs [B,H,N,d] of out_dtype, fully overwritten.
  *   workspace: device memory of at least dsa_attn_bwd_workspace_bytes(shape, kmax)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
- *   Precision with bf16 inputs: dV = P^T dO runs on fp16 matrix cores (P in [0,1]
- *   rounded to fp16, dO converted to fp16: exact for |dO| < 65504, a precondition
- *   like the one on V in dsa_attn_fwd); products with dS use a bf16 hi+lo pair
+ *   Precision with bf16 inputs: dV = P^T dO and dP = dO V^T run on fp16 matrix
+ *   cores (P in [0,1] rounded to fp16; dO converted to fp16 after multiplying it
+ *   by 2^s, one power of two per (b, h) that puts the head's largest |dO| in
+ *   [2^14, 2^15), so the conversion is exact for every element within a factor
+ *   2^31 of that maximum, whatever the size of the gradients; the products are
+ *   scaled back by 2^-s in fp32, exactly); products with dS use a bf16 hi+lo pair
  *   (two matrix-core passes), so their accuracy does not depend on the scale of dS.
  *   The same device-side robustness rules as dsa_attn_fwd apply.
  */
