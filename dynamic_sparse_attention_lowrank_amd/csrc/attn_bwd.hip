@@ -435,18 +435,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  if (n > 0) request(list[e0], q0, g0, st0);
+  // the block's query tiles, 64 list entries per vector load (no scalar-load wait per tile)
+  IdList ids;
+  ids.init(list + e0, n, g.NB, lane);
+  if (n > 0) request(ids.next(lane), q0, g0, st0);
   dma_wait();
   __syncthreads();
   // two tiles per trip so that every LDS buffer is a distinct object (the next
   // tile's direct loads never alias the reads of the current one)
   for (int e = 0; e < n; e += 2) {
-    if (e + 1 < n) request(list[e0 + e + 1], q1, g1, st1);
+    if (e + 1 < n) request(ids.next(lane), q1, g1, st1);
     compute(q0, g0, st0);
     dma_wait();
     __syncthreads();
     if (e + 1 >= n) break;
-    if (e + 2 < n) request(list[e0 + e + 2], q0, g0, st0);
+    if (e + 2 < n) request(ids.next(lane), q0, g0, st0);
     compute(q1, g1, st1);
     dma_wait();
     __syncthreads();
@@ -632,14 +635,9 @@ void bwd_dq_kernel(BwdArgs a) {
   };
 
   // the kept blocks in idx order, invalid entries skipped (wave-uniform)
-  int slot = 0;
-  auto next_valid = [&]() -> int {
-    while (slot < kk) {
-      const int b = irow[slot++];
-      if ((unsigned)b < (unsigned)g.NB) return b;
-    }
-    return -1;
-  };
+  IdList ids;
+  ids.init(irow, kk, g.NB, lane);
+  auto next_valid = [&]() -> int { return ids.next(lane); };
   int bcur = next_valid();
   if (bcur >= 0) request(bcur, k0, v0);
   dma_wait();

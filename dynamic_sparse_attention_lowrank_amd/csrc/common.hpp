@@ -198,6 +198,38 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A tile's list of kept block ids, read by the whole wave in order: 64 entries
+// per vector load (lane i holds entry base + i) and handed out one at a time by
+// v_readlane, so the block loop never waits on a scalar memory load.  Entries
+// outside [0, nb) are skipped.  Must be used with the full wave active.
+struct IdList {
+  const int* p;
+  int n, nb, base, val;
+  uint64_t mask;                              // entries of the current 64 not yet handed out
+  __device__ __forceinline__ void fill(int lane) {
+    val = base + lane < n ? p[base + lane] : -1;
+    mask = ballot((unsigned)val < (unsigned)nb);
+  }
+  __device__ __forceinline__ void init(const int* list, int count, int nblocks, int lane) {
+    p = list;
+    n = count;
+    nb = nblocks;
+    base = 0;
+    fill(lane);
+  }
+  // next valid id, or -1 at the end (wave-uniform)
+  __device__ __forceinline__ int next(int lane) {
+    while (mask == 0) {
+      base += 64;
+      if (base >= n) return -1;
+      fill(lane);
+    }
+    const int b = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    return __builtin_amdgcn_readlane(val, b);
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
