@@ -450,6 +450,62 @@ def summarize(root: str):
         with open(os.path.join(prof, f"traffic_{kname}_{wl_name}.txt"), "w") as fh:
             fh.write("\n".join(body) + "\n")
     print(f"wrote profiles for {wl_name} (source_hash {src_hash}); current sources {source_hash()}")
+    summarize_counters(root, wl_name, src_hash)
+
+
+# per attention kernel: counts of SQ / TA / TCP events per dispatch, and the same
+# per (wave, block) unit -- one wave's 32-key half of one kept block (forward), one
+# wave's 16 keys against one query tile (dK/dV) or its 16 queries against one kept
+# block (dQ) -- so that instruction mixes and unit busy times compare across kernels
+_UNITS = {"attn_fwd_kernel": 2, "bwd_dkdv_kernel": 4, "bwd_dq_kernel": 4}
+
+
+def summarize_counters(root: str, wl_name: str, src_hash: str):
+    """profiles/counters_<workload>.md from the --pmc runs under DIR/counters_* (each
+    with cmd.txt and out.json like the traffic runs), for the three attention kernels."""
+    import glob
+    subs = sorted(glob.glob(os.path.join(root, "counters_*")))
+    if not subs:
+        return
+    vals, cmds, pairs = {}, [], None
+    for sub in subs:
+        cmd, o = _read_run(sub)
+        if o["source_hash"] != src_hash:
+            raise SystemExit(f"{sub} comes from sources {o['source_hash']}, the other runs from {src_hash}")
+        cmds.append(cmd)
+        pairs = o["counted_flop"]["pairs"]
+        import csv
+        for f in sorted(glob.glob(os.path.join(sub, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                label = _kernel_label(r["Kernel_Name"])
+                kname = label.split("<")[0]
+                if kname not in _UNITS:
+                    continue
+                d = vals.setdefault(label, {}).setdefault(r["Counter_Name"], {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    blocks = pairs / (64 * 64)            # (query tile, kept block) pairs of the workload
+    lines = [f"# Hardware counters of the attention kernels on {wl_name}", "",
+             "Commands (from the repository root, on one MI355X; one rocprofv3 pass each):", ""]
+    lines += ["    " + c for c in cmds]
+    lines += ["", f"Library sources: source_hash {src_hash}.", "",
+              "Per dispatch: the counter summed over all its instances, averaged over the dispatches of "
+              "the run. Per unit: divided by the number of (wave, block) units of one launch -- "
+              f"{blocks:.0f} (query tile, kept block) pairs times the waves that share one pair "
+              "(2 in the forward, 4 in dK/dV and dQ).", ""]
+    names = sorted({c for k in vals.values() for c in k})
+    for label in sorted(vals):
+        units = blocks * _UNITS[label.split("<")[0]]
+        lines += [f"## {label}", "", "| counter | per dispatch | per unit |", "|---|---|---|"]
+        for c in names:
+            if c not in vals[label]:
+                continue
+            v = list(vals[label][c].values())
+            avg = sum(v) / len(v)
+            lines.append(f"| {c} | {avg:.4g} | {avg / units:.1f} |")
+        lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"counters_{wl_name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote profiles/counters_{wl_name}.md")
 
 
 if __name__ == "__main__":
