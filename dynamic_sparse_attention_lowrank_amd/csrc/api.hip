@@ -43,6 +43,12 @@ dsa_status derive(const dsa_shape* s, Derived* out) {
   g.tt = s->tt; g.th = s->th; g.tw = s->tw;
   g.gt = s->Lt / s->tt; g.gh = s->Lh / s->th; g.gw = s->Lw / s->tw;
   g.N = (int)N; g.T = (int)T; g.NB = (int)NB;
+  auto rcp = [](int64_t d) -> uint32_t { return d == 1 ? 0u : (uint32_t)(((int64_t)1 << 32) / d + (((int64_t)1 << 32) % d != 0)); };
+  g.m_gw = rcp(g.gw);
+  g.m_gwgh = rcp((int64_t)g.gw * g.gh);
+  g.m_tw = rcp(g.tw);
+  g.m_twth = rcp((int64_t)g.tw * g.th);
+  g.fast_tiles = NB <= 65535;
   out->g = g;
   out->BH = (int)BH;
   out->d = s->d;

@@ -149,20 +149,39 @@ struct Geo {
   int tt, th, tw;      // tile extents
   int gt, gh, gw;      // tile grid extents
   int N, T, NB;        // tokens, tokens per tile, tiles
+  // multiply-high reciprocals ceil(2^32 / d) of gw, gw*gh, tw, tw*th (0 for d = 1):
+  // floor(n / d) = mulhi(n, m) exactly when n * (d - 1) < 2^32, which holds for
+  // member indices (n, d <= 64) always and for tile indices when NB <= 65535
+  // (fast_tiles); otherwise tile_base divides.
+  uint32_t m_gw, m_gwgh, m_tw, m_twth;
+  int fast_tiles;
 };
+
+__device__ __forceinline__ int div_rcp(int n, uint32_t m) {
+  return m == 0 ? n : (int)__umulhi((uint32_t)n, m);
+}
 
 // first token of tile j (its (t, y, x) corner)
 __device__ __forceinline__ int tile_base(const Geo& g, int j) {
-  int jx = j % g.gw;
-  int jy = (j / g.gw) % g.gh;
-  int jt = j / (g.gw * g.gh);
+  int jx, jy, jt;
+  if (g.fast_tiles) {
+    const int q = div_rcp(j, g.m_gw);
+    jt = div_rcp(j, g.m_gwgh);
+    jx = j - q * g.gw;
+    jy = q - jt * g.gh;
+  } else {
+    jx = j % g.gw;
+    jy = (j / g.gw) % g.gh;
+    jt = j / (g.gw * g.gh);
+  }
   return ((jt * g.tt) * g.Lh + jy * g.th) * g.Lw + jx * g.tw;
 }
-// offset of the i-th member (ascending token order) from the tile corner
+// offset of the i-th member (ascending token order, 0 <= i < T <= 64) from the tile corner
 __device__ __forceinline__ int member_offset(const Geo& g, int i) {
-  int dx = i % g.tw;
-  int dy = (i / g.tw) % g.th;
-  int dt = i / (g.tw * g.th);
+  const int q = div_rcp(i, g.m_tw);
+  const int dt = div_rcp(i, g.m_twth);
+  const int dx = i - q * g.tw;
+  const int dy = q - dt * g.th;
   return (dt * g.Lh + dy) * g.Lw + dx;
 }
 
