@@ -12,7 +12,10 @@ Prints one JSON line.  `value` is attended TFLOP/s of the whole step with the
 attended work counted as 4*d FLOP per (query, key) pair forward and 10*d
 backward; `roofline` describes the dominant kernel, timed with HIP events on
 the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload (rank 0, one GPU only).
+sample of the same workload (rank 0, one GPU only).  `phase_stats_ms` gives the
+median / min / max of every phase over the timed steps, `fwd_cold` the forward
+alone after a 512 MiB cache-evicting write (L2 and memory-attached cache cold),
+`clocks` the engine / memory clock levels read from sysfs before and after.
 """
 from __future__ import annotations
 
@@ -23,6 +26,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -41,6 +46,8 @@ def parse():
     ap.add_argument("--workload", default="train_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="repetitions of the forward alone after a 512 MiB cache-evicting write")
     ap.add_argument("--score-matrix", action="store_true",
                     help="predict (writes the NB x NB scores) then select, instead of the fused entry point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -51,6 +58,42 @@ def parse():
                          "(DIR/trace, DIR/fetch, DIR/write, each with the bench JSON line in out.json "
                          "and the command in cmd.txt)")
     return ap.parse_args()
+
+
+def stats(v):
+    """median / min / max of a list of times in ms"""
+    import numpy as np
+    return {"median": round(float(np.median(v)), 4), "min": round(float(min(v)), 4), "max": round(float(max(v)), 4)}
+
+
+def read_clocks():
+    """Current engine and memory clock levels (MHz) of each GPU from sysfs, or None
+    where the files are not readable."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        card = {}
+        for name in ("sclk", "mclk"):
+            try:
+                for line in open(os.path.join(dev, f"pp_dpm_{name}")):
+                    if "*" in line:
+                        card[name] = int("".join(ch for ch in line.split(":")[1] if ch.isdigit()))
+            except (OSError, ValueError, IndexError):
+                pass
+        if card:
+            out[os.path.basename(os.path.dirname(dev))] = card
+    return out or None
+
+
+def pct_at_clock(tflops, c0, c1):
+    """Percentage of the bf16 matrix peak scaled to the mean engine clock read before
+    and after the timed region (the published peak assumes 2.4 GHz), or None."""
+    vals = [c["sclk"] for c in (c0 or {}).values() if "sclk" in c] + \
+           [c["sclk"] for c in (c1 or {}).values() if "sclk" in c]
+    if not vals:
+        return None
+    mhz = sum(vals) / len(vals)
+    return round(100 * tflops / (BF16_PEAK_TFLOPS * mhz / 2400.0), 2)
 
 
 def source_hash() -> str:
@@ -207,12 +250,14 @@ def main():
     # launch stream (torch's current stream) bracket every phase of every step
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    clocks_start = read_clocks()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    phase_ms = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
+    per_step = {p: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, p in enumerate(phases)}
+    phase_ms = {p: sum(v) / args.steps for p, v in per_step.items()}
     span_ms = events[0][0].elapsed_time(events[-1][-1]) / args.steps
 
     # stage-one predictor training signal on the same inputs, timed on its own (not
@@ -251,6 +296,23 @@ def main():
     rope_bytes = 2.0 * (Q.numel() * Q.element_size() + K.numel() * K.element_size() +
                         dQ.numel() * dQ.element_size() + dK.numel() * dK.element_size())
     del rq, rk
+
+    # the forward alone with cold caches: before each repetition a 512 MiB write
+    # (twice the 256 MB memory-attached cache, and far above the L2s) evicts what
+    # the previous repetition left; the in-step phase times above are the warm ones
+    flush = torch.empty(512 << 20, device=dev, dtype=torch.uint8)
+    cold = []
+    for i in range(args.cold_reps + 1):
+        flush.fill_(i & 0xFF)
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ce[0].record()
+        dsa.attn_fwd(Q, K, V, idx, kdev, lay, out=(O, LSE), workspace=fws)
+        ce[1].record()
+        torch.cuda.synchronize()
+        if i:                                           # the first one only sets the pattern up
+            cold.append(ce[0].elapsed_time(ce[1]))
+    del flush
+    clocks_end = read_clocks()
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -297,8 +359,14 @@ def main():
                    "blocks": NB, "rank": r, "k": kmax, "keep_percent": list(wl.keep_percent)},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "fwd": {"ms": round(phase_ms["fwd"], 4), "tflops": round(fwd_tflops, 2),
-                "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2)},
+                "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2),
+                "pct_bf16_peak_at_measured_sclk": pct_at_clock(fwd_tflops, clocks_start, clocks_end)},
         "phase_ms": {p: round(v, 4) for p, v in phase_ms.items() if p != "-"},
+        "phase_stats_ms": {p: stats(v) for p, v in per_step.items() if p != "-"},
+        "fwd_cold": dict(stats(cold), reps=len(cold), flush_mib=512,
+                         tflops_at_median=round(flop_fwd / (float(np.median(cold)) * 1e-3) / 1e12, 2))
+                    if cold else None,
+        "clocks": {"start": clocks_start, "end": clocks_end},
         "event_ms_per_step": round(span_ms, 4),
         "counted_flop": {"fwd": flop_fwd, "bwd": flop_bwd, "pairs": pairs},
         "roofline": roofline,
