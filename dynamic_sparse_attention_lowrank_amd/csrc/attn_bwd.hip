@@ -170,7 +170,7 @@ __global__ __launch_bounds__(1024) void rev_scan_kernel(BwdArgs a) {
   part[threadIdx.x] = s;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {        // Hillis-Steele inclusive scan
-    const int v = threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+    const int v = (int)threadIdx.x >= d ? part[threadIdx.x - d] : 0;
     __syncthreads();
     part[threadIdx.x] += v;
     __syncthreads();
@@ -222,6 +222,10 @@ __global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
 // the prepare phase, V converted when loaded, P in [0,1] rounded to fp16; both
 // products are multiplied by 2^-s in fp32, exactly); S = Q K^T
 // and dK = dS^T Q stay bf16, dS as a hi+lo pair.  fp32 inputs use fp32 throughout.
+// two waves per SIMD for 16-bit inputs; the fp32 variants (parity checks only)
+// need more than 256 registers and run at one
+template <typename T> constexpr int kWavesPerSimd = sizeof(T) == 2 ? 2 : 1;
+
 template <typename T> struct GradType;
 template <> struct GradType<bf16> { typedef f16 type; };
 template <> struct GradType<float> { typedef float type; };
@@ -246,7 +250,7 @@ __device__ __forceinline__ f32x8 to_grad_frag(f32x8 v, float*) { return v; }
 //                                  (the k-slots follow the result's row order),
 //                                  B = dO / Q read transposed (ds_read_b64_tr_b16)
 template <typename T, int D, bool FULL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<T>, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
   typedef typename GradType<T>::type G;
   constexpr int W = 4;
@@ -481,7 +485,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 //   dQ^T += K^T dS^T                   B = dS^T straight from the S^T registers (bf16
 //                                      hi+lo), A = K read transposed (ds_read_b64_tr_b16)
 template <typename T, int D, bool FULL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<T>, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int W = 4;
   using C = TileCfg<T, D>;

@@ -378,7 +378,6 @@ void attn_fwd_kernel(FwdArgs a) {
 
   const size_t head_off = (size_t)bh * g.N * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(a.Q) + head_off;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(a.K) + head_off;
   const int* __restrict__ irow = a.idx + ((size_t)bh * g.NB + tau) * a.kmax;
   int kk = a.kvec[bh];
   kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
@@ -393,9 +392,6 @@ void attn_fwd_kernel(FwdArgs a) {
   }
   __syncthreads();
 
-  const int kr = 32 * w + l32;                // this lane's key row inside the wave's half
-  const bool k_ok = kr < g.T;
-  const int koff = k_ok ? member_offset(g, kr) : 0;
   const int kvalid = g.T - 32 * w;            // valid keys in this wave's half (may be <= 0)
 
   WaveState<T, D> st;

@@ -36,7 +36,7 @@ __device__ __forceinline__ void pool_project_body(const PredictArgs& a) {
   const Geo g = a.g;
   const int BH = a.B * a.H;
   const int per = BH * g.NB;
-  const int which = blockIdx.x >= per;         // 0: Q, 1: K
+  const int which = (int)blockIdx.x >= per;    // 0: Q, 1: K
   const int L = blockIdx.x - which * per;
   const int bh = L / g.NB;
   const int tau = L - bh * g.NB;
