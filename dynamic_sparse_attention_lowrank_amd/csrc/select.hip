@@ -11,7 +11,9 @@
 // slot on rows of up to 1024 blocks, per-lane vector counts and one DPP wave sum on
 // longer rows), then a single ascending sweep emits: own block, keys > T, and the
 // lowest-index keys == T until k are taken.  Rows of up to 8192 blocks live in
-// registers; longer rows are re-read from memory on each step (L2-resident).
+// registers; rows of up to 16,384 blocks are formed once into LDS (one wave per
+// work-group, at most 64 KB); longer rows are re-read from memory on each step
+// (L2-resident).
 //
 // The fused variant (dsa_predict_select) computes each row's scores from the
 // pooled features instead of reading a stored score matrix (bit-identical scores),
@@ -102,6 +104,36 @@ struct Row {
   }
 };
 
+// Rows of 8,193 to 16,384 blocks: keys in LDS, four slots of one lane per 16-byte
+// word (slot 4q+e of lane l at word 64q+l, element e), so one pass of the search is
+// one ds_read_b128 per four slots.  nslots is a multiple of 4; slots past the row
+// hold 0 (not a candidate).
+constexpr int kLdsMaxSlots = 256;             // 16,384 blocks, 64 KB of keys
+struct LdsRow {
+  const uint32_t* lk;
+  int NB, tau, lane, nslots;
+  __device__ __forceinline__ int count_ge(uint32_t t) const {
+    const u32x4* p = reinterpret_cast<const u32x4*>(lk) + lane;
+    int cnt = 0;
+    for (int q = 0; q < nslots / 4; ++q) {
+      const u32x4 v = p[64 * q];
+      cnt += (v[0] >= t ? 1 : 0) + (v[1] >= t ? 1 : 0) + (v[2] >= t ? 1 : 0) + (v[3] >= t ? 1 : 0);
+    }
+    return wave_sum(cnt);
+  }
+  __device__ __forceinline__ uint32_t at(int i) const { return lk[((i >> 2) * 64 + lane) * 4 + (i & 3)]; }
+};
+template <typename KeyFn>
+__device__ __forceinline__ void fill_lds(uint32_t* lk, int nslots, int lane, const KeyFn& key) {
+  for (int q = 0; q < nslots / 4; ++q) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = key(4 * q + e, lane);
+    reinterpret_cast<u32x4*>(lk)[64 * q + lane] = v;
+  }
+}
+__host__ __device__ inline int lds_slots(int NB) { return ((NB + 63) / 64 + 3) & ~3; }
+
 template <typename R>
 __device__ __forceinline__ void sweep_slot(const R& rw, int i, int l, bool own_lane, uint32_t T, int kp,
                                            int need_eq, int& taken, int& eq_seen, int32_t* __restrict__ out,
@@ -179,6 +211,35 @@ hipError_t launch_sel(const SelectArgs& a, hipStream_t s) {
   const int rows = a.BH * a.NB;
   const int grid = (rows + kWaves - 1) / kWaves;
   hipLaunchKernelGGL((select_kernel<SLOTS>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+// one wave per row, keys in LDS (rows of 8,193 to 16,384 blocks)
+__global__ __launch_bounds__(64) void select_lds_kernel(SelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_keys[];
+  const int lane = threadIdx.x;
+  const int rowid = blockIdx.x;
+  const int NB = a.NB;
+  const int bh = rowid / NB;
+  const int tau = rowid - bh * NB;
+  int k = a.kvec[bh];
+  k = k < 1 ? 1 : (k > a.kmax ? a.kmax : k);
+  int32_t* __restrict__ out = a.idx + (size_t)rowid * a.kmax;
+  Row<0> src;
+  src.s = a.S + (size_t)rowid * NB;
+  src.NB = NB;
+  src.tau = tau;
+  src.lane = lane;
+  const int nslots = lds_slots(NB);
+  fill_lds(lds_keys, nslots, lane, [&](int i, int l) { return src.load(i, l); });
+  __syncthreads();
+  LdsRow rw{lds_keys, NB, tau, lane, nslots};
+  select_row<0>(rw, k - 1, k, out, a.kmax);
+}
+
+hipError_t launch_sel_lds(const SelectArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)lds_slots(a.NB) * 64 * sizeof(uint32_t);
+  hipLaunchKernelGGL(select_lds_kernel, dim3(a.BH * a.NB), dim3(64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -282,6 +343,40 @@ __global__ __launch_bounds__(64 * kWaves) void fused_select_kernel(FusedSelectAr
   }
 }
 
+// one wave per row, keys formed once into LDS (rows of 8,193 to 16,384 blocks)
+template <int RM, bool EXACT>
+__global__ __launch_bounds__(64) void fused_select_lds_kernel(FusedSelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_keys[];
+  const int lane = threadIdx.x;
+  const int rowid = blockIdx.x;
+  const int NB = a.NB;
+  const int bh = rowid / NB;
+  const int tau = rowid - bh * NB;
+  int k = a.kvec[bh];
+  k = k < 1 ? 1 : (k > a.kmax ? a.kmax : k);
+  int32_t* __restrict__ out = a.idx + (size_t)rowid * a.kmax;
+  PooledRow<RM, EXACT> p;
+  p.kb = a.Kbar + (size_t)bh * NB * a.r;
+  const float* qb = a.Qbar + (size_t)rowid * a.r + fresh_lane(0);
+#pragma unroll
+  for (int c = 0; c < RM; ++c) p.qv[c] = c < a.r ? qb[c] : 0.f;
+  p.r = a.r;
+  p.NB = NB;
+  p.tau = tau;
+  const int nslots = lds_slots(NB);
+  fill_lds(lds_keys, nslots, lane, [&](int i, int l) { return p.key(i, l); });
+  __syncthreads();
+  LdsRow rw{lds_keys, NB, tau, lane, nslots};
+  select_row<0>(rw, k - 1, k, out, a.kmax);
+}
+
+template <int RM, bool EXACT>
+hipError_t launch_fsel_lds(const FusedSelectArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)lds_slots(a.NB) * 64 * sizeof(uint32_t);
+  hipLaunchKernelGGL((fused_select_lds_kernel<RM, EXACT>), dim3(a.BH * a.NB), dim3(64), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int SLOTS, int RM, bool EXACT>
 hipError_t launch_fsel(const FusedSelectArgs& a, hipStream_t s) {
   const int rows = a.BH * a.NB;
@@ -300,6 +395,7 @@ hipError_t launch_fsel_rm(const FusedSelectArgs& a, hipStream_t s) {
   if (slots <= 32) return launch_fsel<32, RM, EXACT>(a, s);
   if (slots <= 64) return launch_fsel<64, RM, EXACT>(a, s);
   if (slots <= 128) return launch_fsel<128, RM, EXACT>(a, s);
+  if (slots <= kLdsMaxSlots) return launch_fsel_lds<RM, EXACT>(a, s);
   return launch_fsel<0, RM, EXACT>(a, s);
 }
 
@@ -322,6 +418,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (slots <= 32) return launch_sel<32>(a, s);
   if (slots <= 64) return launch_sel<64>(a, s);
   if (slots <= 128) return launch_sel<128>(a, s);
+  if (slots <= kLdsMaxSlots) return launch_sel_lds(a, s);
   return launch_sel<0>(a, s);
 }
 
