@@ -10,9 +10,11 @@
 // then one d x r product), which reads Q and K exactly once.  All sums are fp32.
 //
 // Kernel 1 (pool_project): one work-group per (tensor, head, tile); 16-byte
-//   coalesced row loads, fp32 column sums, LDS tree over token groups in a fixed
-//   order, then the d x r projection (optionally also stores the tile means, and
-//   with no Qbar/Kbar output only those, for the predictor's training signal).
+//   coalesced row loads (all of a thread's rows in flight at once), fp32 column
+//   sums, LDS tree over token groups in a fixed order, then the d x r projection
+//   split over all threads by d segments, summed in a fixed order (optionally also
+//   stores the tile means, and with no Qbar/Kbar output only those, for the
+//   predictor's training signal).
 // Kernel 2 (scores): one work-group per (head, 64 query tiles, 256 key blocks);
 //   a thread owns one key block, keeps its Kbar row in registers and writes 64
 //   coalesced scores.  Bound by writing S.
@@ -51,9 +53,19 @@ __device__ __forceinline__ void pool_project_body(const PredictArgs& a) {
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
   const int base = tile_base(g, tau);
-  for (int i = rsub; i < g.T; i += RPG) {
-    const u32x4 ch = *reinterpret_cast<const u32x4*>(X + (size_t)(base + member_offset(g, i)) * D + c * CE);
-    const T* v = reinterpret_cast<const T*>(&ch);
+  // rows rsub, rsub + RPG, ... (T <= 64): every load issued before the first add;
+  // absent rows load zeros, which leave the sums unchanged
+  constexpr int MAXR = (64 + RPG - 1) / RPG;
+  u32x4 ch[MAXR];
+#pragma unroll
+  for (int q = 0; q < MAXR; ++q) {
+    const int i = rsub + q * RPG;
+    ch[q] = i < g.T ? *reinterpret_cast<const u32x4*>(X + (size_t)(base + member_offset(g, i)) * D + c * CE)
+                    : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int q = 0; q < MAXR; ++q) {
+    const T* v = reinterpret_cast<const T*>(&ch[q]);
 #pragma unroll
     for (int e = 0; e < CE; ++e) acc[e] += to_f32(v[e]);
   }
@@ -69,10 +81,21 @@ __device__ __forceinline__ void pool_project_body(const PredictArgs& a) {
   }
   if (!out) return;                            // tile means only
   __syncthreads();
+  // projection on all threads: column cc of W over one of nseg contiguous d
+  // segments, then the segments summed in order (rp = r rounded up to 16/32/64)
+  const int rp = a.r <= 16 ? 16 : (a.r <= 32 ? 32 : 64);
+  const int nseg = kPoolThreads / rp;
+  const int cc = tid % rp, sg = tid / rp, len = D / nseg;
+  float o = 0.f;
+  if (cc < a.r) {
+    for (int e = sg * len; e < (sg + 1) * len; ++e) o = fmaf(xmean[e], to_f32(W[e * a.r + cc]), o);
+  }
+  red[sg * rp + cc] = o;                       // red is free once xmean is formed
+  __syncthreads();
   if (tid < a.r) {
-    float o = 0.f;
-    for (int e = 0; e < D; ++e) o = fmaf(xmean[e], to_f32(W[e * a.r + tid]), o);
-    out[((size_t)bh * g.NB + tau) * a.r + tid] = o;
+    float t = 0.f;
+    for (int q = 0; q < nseg; ++q) t += red[q * rp + tid];
+    out[((size_t)bh * g.NB + tau) * a.r + tid] = t;
   }
 }
 
