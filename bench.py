@@ -302,7 +302,7 @@ def main():
     # the previous repetition left; the in-step phase times above are the warm ones
     flush = torch.empty(512 << 20, device=dev, dtype=torch.uint8)
     cold = []
-    for i in range(args.cold_reps + 1):
+    for i in range(args.cold_reps + 1 if args.cold_reps > 0 else 0):
         flush.fill_(i & 0xFF)
         ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ce[0].record()
