@@ -26,6 +26,7 @@ import math
 import os
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -106,10 +107,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
+def load_traffic(kernel: str, workload: str, prof_dir: Optional[str] = None):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
     taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    path = os.path.join(prof_dir or os.path.join(ROOT, "profiles"), f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -439,7 +440,7 @@ def _counter_rows(sub: str, counter: str):
     return rows
 
 
-def summarize(root: str):
+def summarize(root: str, prof_dir: Optional[str] = None):
     """Write profiles/<workload>_kernel_trace.md from a `--kernel-trace --stats` run
     and profiles/traffic_<kernel>_<workload>.txt from one FETCH_SIZE and one
     WRITE_SIZE `--pmc` run, each counter scaled by what it reads for the
@@ -447,7 +448,7 @@ def summarize(root: str):
     that many bytes read and written)."""
     import csv
     import glob
-    prof = os.path.join(ROOT, "profiles")
+    prof = prof_dir or os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
 
     cmd, out = _read_run(os.path.join(root, "trace"))
@@ -518,7 +519,7 @@ def summarize(root: str):
         with open(os.path.join(prof, f"traffic_{kname}_{wl_name}.txt"), "w") as fh:
             fh.write("\n".join(body) + "\n")
     print(f"wrote profiles for {wl_name} (source_hash {src_hash}); current sources {source_hash()}")
-    summarize_counters(root, wl_name, src_hash)
+    summarize_counters(root, wl_name, src_hash, prof)
 
 
 # per attention kernel: counts of SQ / TA / TCP events per dispatch, and the same
@@ -528,7 +529,7 @@ def summarize(root: str):
 _UNITS = {"attn_fwd_kernel": 2, "bwd_dkdv_kernel": 4, "bwd_dq_kernel": 4}
 
 
-def summarize_counters(root: str, wl_name: str, src_hash: str):
+def summarize_counters(root: str, wl_name: str, src_hash: str, prof: str):
     """profiles/counters_<workload>.md from the --pmc runs under DIR/counters_* (each
     with cmd.txt and out.json like the traffic runs), for the three attention kernels."""
     import glob
@@ -571,7 +572,7 @@ def summarize_counters(root: str, wl_name: str, src_hash: str):
             avg = sum(v) / len(v)
             lines.append(f"| {c} | {avg:.4g} | {avg / units:.1f} |")
         lines.append("")
-    with open(os.path.join(ROOT, "profiles", f"counters_{wl_name}.md"), "w") as fh:
+    with open(os.path.join(prof, f"counters_{wl_name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote profiles/counters_{wl_name}.md")
 
