@@ -107,6 +107,9 @@ DSA_API dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q,
  *   S: [B,H,NB,NB] float32.  k: device int32 [B*H].  idx: output [B,H,NB,kmax] int32.
  *   1 <= kmax <= NB is required (DSA_ERR_K).  A device value k outside
  *   [1, kmax] is clamped into that range.
+ *   Cost: one wave per row; a row's keys are held in registers up to NB = 8192,
+ *   in LDS up to NB = 16384, and re-read on each of the search's 33 passes above
+ *   that (correct at any NB, but slow for very long rows).
  */
 DSA_API dsa_status dsa_select(const dsa_shape* shape, const float* S, const int32_t* k, int32_t kmax,
                       int32_t* idx, hipStream_t stream);
