@@ -125,10 +125,14 @@ def fourier_features(wl: Workload, device) -> torch.Tensor:
     beta = uniform(wl.seed, tag_of("rff.beta"), 0, H * nf, device).view(H, nf) * (2.0 * math.pi)
     proj = normal(wl.seed, tag_of("rff.proj"), H * nf * d, device).view(H, nf, d)
     Lt, Lh, Lw = wl.latent
-    t = torch.arange(Lt, device=device, dtype=torch.float64)
-    y = torch.arange(Lh, device=device, dtype=torch.float64)
-    x = torch.arange(Lw, device=device, dtype=torch.float64)
-    coords = torch.stack(torch.meshgrid(t, y, x, indexing="ij"), dim=-1).reshape(-1, 3)   # [N, 3]
+    # integer latent coordinates of every token, row-major (t, y, x); written column
+    # by column (no tensor concatenation: a float64 concatenation kernel crashed
+    # under a hardware-counter profiler)
+    n = torch.arange(wl.N, device=device, dtype=torch.int64)
+    coords = torch.empty(wl.N, 3, device=device, dtype=torch.float64)                   # [N, 3]
+    coords[:, 0] = (n // (Lh * Lw)).to(torch.float64)
+    coords[:, 1] = ((n // Lw) % Lh).to(torch.float64)
+    coords[:, 2] = (n % Lw).to(torch.float64)
     F = torch.empty(H, wl.N, d, dtype=torch.float64, device=device)
     for h in range(H):
         phase = coords @ omega[h].T + beta[h]                                                # [N, 32]
@@ -203,6 +207,8 @@ def _normal_slice(seed: int, tag: int, start: int, count: int, device) -> torch.
         u = uniform(seed, tag, start + 2 * p0, 2 * pc, device).view(pc, 2)
         rad = torch.sqrt(-2.0 * torch.log1p(-u[:, 0]))
         ang = (2.0 * math.pi) * u[:, 1]
-        out[2 * p0: 2 * (p0 + pc)] = torch.stack((rad * torch.cos(ang), rad * torch.sin(ang)), 1).reshape(-1)
+        pair = out[2 * p0: 2 * (p0 + pc)].view(pc, 2)
+        pair[:, 0] = rad * torch.cos(ang)
+        pair[:, 1] = rad * torch.sin(ang)
         p0 += pc
     return out

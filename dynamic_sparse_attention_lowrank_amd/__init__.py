@@ -143,12 +143,58 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _expect(name: str, t, shape, dtypes) -> None:
+    """Shape and dtype of one argument, checked before anything reaches the library
+    (a short or mis-typed buffer would otherwise be read or written past its end)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(name: str, t, need: int) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D uint8 tensor")
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {need} needed")
+
+
 def _dev(*ts: torch.Tensor) -> None:
+    """Every tensor on the same GPU (checked after the shapes and dtypes)."""
+    dev = None
     for t in ts:
         if not t.is_cuda:
             raise ValueError("all tensors must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+
+
+_IO = (torch.float32, torch.bfloat16)
+
+
+def _qkv(layout: "Layout", Q: torch.Tensor, **named: torch.Tensor):
+    """Q is [B, H, N, d] float32 or bfloat16 and every other named tensor matches it."""
+    if not isinstance(Q, torch.Tensor) or Q.dim() != 4:
+        raise ValueError("Q must be a [B, H, N, d] tensor")
+    _expect("Q", Q, Q.shape, _IO)
+    if Q.shape[2] != layout.N:
+        raise ValueError(f"Q has N={Q.shape[2]} tokens but the latent {layout.latent} holds {layout.N}")
+    for n, t in named.items():
+        _expect(n, t, Q.shape, Q.dtype)
+    return Q.shape
+
+
+def _kvec(k: torch.Tensor, B: int, H: int) -> None:
+    _expect("k", k, (B * H,), torch.int32)
 
 
 def _stream() -> int:
@@ -160,19 +206,32 @@ def _check(status: int) -> None:
         raise DsaError(status, _L().dsa_status_string(status).decode())
 
 
+def _rank(Wq: torch.Tensor, Wk: torch.Tensor, H: int, d: int, dtype) -> int:
+    """Wq, Wk are [H, d, r] in the I/O dtype; returns r."""
+    if not isinstance(Wq, torch.Tensor) or Wq.dim() != 3:
+        raise ValueError("Wq must be an [H, d, r] tensor")
+    r = Wq.shape[-1]
+    _expect("Wq", Wq, (H, d, r), dtype)
+    _expect("Wk", Wk, (H, d, r), dtype)
+    return r
+
+
 def predict(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, layout: Layout,
             out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Low-rank predictor: returns (Qbar, Kbar, S) as float32 [B,H,NB,r], [B,H,NB,r], [B,H,NB,NB]."""
-    _dev(Q, K, Wq, Wk)
-    sh = _shape(Q, layout)
-    B, H = Q.shape[:2]
-    r = Wq.shape[-1]
+    B, H, N, d = _qkv(layout, Q, K=K)
+    r = _rank(Wq, Wk, H, d, Q.dtype)
     if out is None:
         Qbar = torch.empty(B, H, layout.NB, r, device=Q.device, dtype=torch.float32)
         Kbar = torch.empty_like(Qbar)
         S = torch.empty(B, H, layout.NB, layout.NB, device=Q.device, dtype=torch.float32)
     else:
         Qbar, Kbar, S = out
+    _expect("Qbar", Qbar, (B, H, layout.NB, r), torch.float32)
+    _expect("Kbar", Kbar, (B, H, layout.NB, r), torch.float32)
+    _expect("S", S, (B, H, layout.NB, layout.NB), torch.float32)
+    _dev(Q, K, Wq, Wk, Qbar, Kbar, S)
+    sh = _shape(Q, layout)
     _check(_L().dsa_predict(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(Qbar), _ptr(Kbar),
                            _ptr(S), _stream()))
     return Qbar, Kbar, S
@@ -181,10 +240,15 @@ def predict(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor
 def select(S: torch.Tensor, k: torch.Tensor, kmax: int, layout: Layout, d: int = 128,
            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Top-k key blocks per query tile: idx int32 [B,H,NB,kmax], ascending, -1 padded."""
-    _dev(S, k)
+    if not isinstance(S, torch.Tensor) or S.dim() != 4:
+        raise ValueError("S must be a [B, H, NB, NB] tensor")
     B, H = S.shape[:2]
-    sh = Shape(B, H, d, *layout.latent, *layout.tile, F32)
+    _expect("S", S, (B, H, layout.NB, layout.NB), torch.float32)
+    _kvec(k, B, H)
     idx = out if out is not None else torch.empty(B, H, layout.NB, kmax, device=S.device, dtype=torch.int32)
+    _expect("idx", idx, (B, H, layout.NB, kmax), torch.int32)
+    _dev(S, k, idx)
+    sh = Shape(B, H, d, *layout.latent, *layout.tile, F32)
     _check(_L().dsa_select(ctypes.byref(sh), _ptr(S), _ptr(k), kmax, _ptr(idx), _stream()))
     return idx
 
@@ -192,16 +256,20 @@ def select(S: torch.Tensor, k: torch.Tensor, kmax: int, layout: Layout, d: int =
 def predict_select(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, k: torch.Tensor, kmax: int,
                    layout: Layout, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Predictor and top-k selection without the score matrix: returns (Qbar, Kbar, idx)."""
-    _dev(Q, K, Wq, Wk, k)
-    sh = _shape(Q, layout)
-    B, H = Q.shape[:2]
-    r = Wq.shape[-1]
+    B, H, N, d = _qkv(layout, Q, K=K)
+    r = _rank(Wq, Wk, H, d, Q.dtype)
+    _kvec(k, B, H)
     if out is None:
         Qbar = torch.empty(B, H, layout.NB, r, device=Q.device, dtype=torch.float32)
         Kbar = torch.empty_like(Qbar)
         idx = torch.empty(B, H, layout.NB, kmax, device=Q.device, dtype=torch.int32)
     else:
         Qbar, Kbar, idx = out
+    _expect("Qbar", Qbar, (B, H, layout.NB, r), torch.float32)
+    _expect("Kbar", Kbar, (B, H, layout.NB, r), torch.float32)
+    _expect("idx", idx, (B, H, layout.NB, kmax), torch.int32)
+    _dev(Q, K, Wq, Wk, k, Qbar, Kbar, idx)
+    sh = _shape(Q, layout)
     _check(_L().dsa_predict_select(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(k), kmax,
                                    _ptr(Qbar), _ptr(Kbar), _ptr(idx), _stream()))
     return Qbar, Kbar, idx
@@ -210,11 +278,11 @@ def predict_select(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch
 def rope3d(X: torch.Tensor, layout: Layout, base: float = 10000.0, offsets: Tuple[int, int, int] = (0, 0, 0),
            inverse: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """3-D rotary positions of X [B,H,N,d] (bf16 or fp32); `out` may be X (in place)."""
-    _dev(X)
-    sh = _shape(X, layout)
+    _qkv(layout, X)
     Y = torch.empty_like(X) if out is None else out
-    if Y.shape != X.shape or Y.dtype != X.dtype or not Y.is_contiguous():
-        raise ValueError("rope3d: out must be a contiguous tensor of X's shape and dtype")
+    _expect("out", Y, X.shape, X.dtype)
+    _dev(X, Y)
+    sh = _shape(X, layout)
     dt = F32 if X.dtype == torch.float32 else BF16
     _check(_L().dsa_rope3d(ctypes.byref(sh), dt, float(base), int(offsets[0]), int(offsets[1]), int(offsets[2]),
                            int(bool(inverse)), _ptr(X), _ptr(Y), _stream()))
@@ -230,19 +298,23 @@ def predictor_grad(Q: torch.Tensor, K: torch.Tensor, Wq: torch.Tensor, Wk: torch
                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                    workspace: Optional[torch.Tensor] = None):
     """Stage-one predictor loss and weight gradients: returns (loss [B,H], dWq [H,d,r], dWk [H,d,r]), fp32."""
-    _dev(Q, K, Wq, Wk)
-    sh = _shape(Q, layout)
-    B, H = Q.shape[:2]
-    r = Wq.shape[-1]
+    B, H, N, d = _qkv(layout, Q, K=K)
+    r = _rank(Wq, Wk, H, d, Q.dtype)
     if out is None:
         loss = torch.empty(B, H, device=Q.device, dtype=torch.float32)
         dWq = torch.empty(Wq.shape, device=Q.device, dtype=torch.float32)
         dWk = torch.empty(Wk.shape, device=Q.device, dtype=torch.float32)
     else:
         loss, dWq, dWk = out
+    _expect("loss", loss, (B, H), torch.float32)
+    _expect("dWq", dWq, (H, d, r), torch.float32)
+    _expect("dWk", dWk, (H, d, r), torch.float32)
+    sh = _shape(Q, layout)
+    need = int(_L().dsa_predictor_grad_workspace_bytes(ctypes.byref(sh)))
     if workspace is None:
-        need = int(_L().dsa_predictor_grad_workspace_bytes(ctypes.byref(sh)))
         workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
+    _workspace("workspace", workspace, need)
+    _dev(Q, K, Wq, Wk, loss, dWq, dWk, workspace)
     _check(_L().dsa_predictor_grad(ctypes.byref(sh), r, _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(loss), _ptr(dWq),
                                    _ptr(dWk), _ptr(workspace), workspace.numel(), _stream()))
     return loss, dWq, dWk
@@ -253,24 +325,37 @@ def fwd_workspace_bytes(Q: torch.Tensor, layout: Layout) -> int:
     return int(_L().dsa_attn_fwd_workspace_bytes(ctypes.byref(sh)))
 
 
+def _idx(idx: torch.Tensor, B: int, H: int, layout: "Layout") -> int:
+    """idx is int32 [B, H, NB, kmax]; returns kmax."""
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 4:
+        raise ValueError("idx must be a [B, H, NB, kmax] tensor")
+    _expect("idx", idx, (B, H, layout.NB, idx.shape[-1]), torch.int32)
+    return idx.shape[-1]
+
+
 def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, k: torch.Tensor, layout: Layout,
              scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
              out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, workspace: Optional[torch.Tensor] = None):
     """Block-sparse attention forward: returns (O [B,H,N,d] out_dtype, LSE [B,H,N] float32)."""
-    _dev(Q, K, V, idx, k)
-    sh = _shape(Q, layout)
-    kmax = idx.shape[-1]
+    B, H, N, d = _qkv(layout, Q, K=K, V=V)
+    kmax = _idx(idx, B, H, layout)
+    _kvec(k, B, H)
     if scale is None:
-        scale = 1.0 / math.sqrt(Q.shape[-1])
+        scale = 1.0 / math.sqrt(d)
     odt = out_dtype or Q.dtype
     if out is None:
         O = torch.empty(Q.shape, device=Q.device, dtype=odt)
         LSE = torch.empty(Q.shape[:3], device=Q.device, dtype=torch.float32)
     else:
         O, LSE = out
+    _expect("O", O, Q.shape, _IO)
+    _expect("LSE", LSE, (B, H, N), torch.float32)
+    sh = _shape(Q, layout)
+    need = int(_L().dsa_attn_fwd_workspace_bytes(ctypes.byref(sh)))
     if workspace is None:
-        need = int(_L().dsa_attn_fwd_workspace_bytes(ctypes.byref(sh)))
         workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
+    _workspace("workspace", workspace, need)
+    _dev(Q, K, V, idx, k, O, LSE, workspace)
     _check(_L().dsa_attn_fwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
                              _io_code(O), _ptr(O), _ptr(LSE), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream()))
@@ -287,13 +372,14 @@ def attn_bwd(Q, K, V, O, dO, LSE, idx, k, layout: Layout, scale: Optional[float]
              out: Optional[Sequence[torch.Tensor]] = None):
     """Block-sparse attention backward (mask fixed): returns (dQ, dK, dV).
 
-    O may be float32 or bfloat16 (the forward output); float32 keeps D = dO . O
-    accurate."""
-    _dev(Q, K, V, O, dO, LSE, idx, k)
-    sh = _shape(Q, layout)
-    kmax = idx.shape[-1]
+    O is the float32 forward output (it enters through D = dO . O)."""
+    B, H, N, d = _qkv(layout, Q, K=K, V=V, dO=dO)
+    _expect("O", O, Q.shape, torch.float32)
+    _expect("LSE", LSE, (B, H, N), torch.float32)
+    kmax = _idx(idx, B, H, layout)
+    _kvec(k, B, H)
     if scale is None:
-        scale = 1.0 / math.sqrt(Q.shape[-1])
+        scale = 1.0 / math.sqrt(d)
     odt = out_dtype or Q.dtype
     if out is None:
         dQ = torch.empty(Q.shape, device=Q.device, dtype=odt)
@@ -301,9 +387,15 @@ def attn_bwd(Q, K, V, O, dO, LSE, idx, k, layout: Layout, scale: Optional[float]
         dV = torch.empty_like(dQ)
     else:
         dQ, dK, dV = out
+    _expect("dQ", dQ, Q.shape, _IO)
+    _expect("dK", dK, Q.shape, dQ.dtype)
+    _expect("dV", dV, Q.shape, dQ.dtype)
+    sh = _shape(Q, layout)
     need = int(_L().dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=Q.device, dtype=torch.uint8)
+    _workspace("workspace", workspace, need)
+    _dev(Q, K, V, O, dO, LSE, idx, k, dQ, dK, dV, workspace)
     _check(_L().dsa_attn_bwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _io_code(O), _ptr(dO), _ptr(LSE),
                             _ptr(idx),
                             _ptr(k), kmax, scale, _io_code(dQ), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
@@ -317,18 +409,28 @@ def _ws_args(workspace: torch.Tensor):
 
 def attn_bwd_prepare(O, dO, idx, k, layout: Layout, workspace: torch.Tensor) -> None:
     """Backward phase 1: D and the reverse block index into ``workspace``."""
-    _dev(O, dO, idx, k, workspace)
+    B, H, N, d = _qkv(layout, dO)
+    _expect("O", O, dO.shape, torch.float32)
+    kmax = _idx(idx, B, H, layout)
+    _kvec(k, B, H)
     sh = _shape(dO, layout)
+    _workspace("workspace", workspace, int(_L().dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax)))
+    _dev(O, dO, idx, k, workspace)
     _check(_L().dsa_attn_bwd_prepare(ctypes.byref(sh), _ptr(O), _io_code(O), _ptr(dO), _ptr(idx), _ptr(k),
-                                    idx.shape[-1], *_ws_args(workspace), _stream()))
+                                    kmax, *_ws_args(workspace), _stream()))
 
 
 def attn_bwd_dkdv(Q, K, V, dO, LSE, kmax: int, layout: Layout, workspace: torch.Tensor, dK: torch.Tensor,
                   dV: torch.Tensor, scale: Optional[float] = None) -> None:
     """Backward phase 2: dK, dV (needs a prepared workspace)."""
-    _dev(Q, K, V, dO, LSE, workspace, dK, dV)
+    B, H, N, d = _qkv(layout, Q, K=K, V=V, dO=dO)
+    _expect("LSE", LSE, (B, H, N), torch.float32)
+    _expect("dK", dK, Q.shape, _IO)
+    _expect("dV", dV, Q.shape, dK.dtype)
     sh = _shape(Q, layout)
-    scale = 1.0 / math.sqrt(Q.shape[-1]) if scale is None else scale
+    _workspace("workspace", workspace, int(_L().dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax)))
+    _dev(Q, K, V, dO, LSE, workspace, dK, dV)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(_L().dsa_attn_bwd_dkdv(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), kmax, scale,
                                  _io_code(dK), _ptr(dK), _ptr(dV), *_ws_args(workspace), _stream()))
 
@@ -336,8 +438,14 @@ def attn_bwd_dkdv(Q, K, V, dO, LSE, kmax: int, layout: Layout, workspace: torch.
 def attn_bwd_dq(Q, K, V, dO, LSE, idx, k, layout: Layout, workspace: torch.Tensor, dQ: torch.Tensor,
                 scale: Optional[float] = None) -> None:
     """Backward phase 3: dQ (needs a prepared workspace)."""
-    _dev(Q, K, V, dO, LSE, idx, k, workspace, dQ)
+    B, H, N, d = _qkv(layout, Q, K=K, V=V, dO=dO)
+    _expect("LSE", LSE, (B, H, N), torch.float32)
+    kmax = _idx(idx, B, H, layout)
+    _kvec(k, B, H)
+    _expect("dQ", dQ, Q.shape, _IO)
     sh = _shape(Q, layout)
-    scale = 1.0 / math.sqrt(Q.shape[-1]) if scale is None else scale
+    _workspace("workspace", workspace, int(_L().dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax)))
+    _dev(Q, K, V, dO, LSE, idx, k, workspace, dQ)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(_L().dsa_attn_bwd_dq(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(idx), _ptr(k),
-                               idx.shape[-1], scale, _io_code(dQ), _ptr(dQ), *_ws_args(workspace), _stream()))
+                               kmax, scale, _io_code(dQ), _ptr(dQ), *_ws_args(workspace), _stream()))

@@ -37,7 +37,10 @@ dsa_status derive(const dsa_shape* s, Derived* out) {
   // blocks) must fit the kernels' signed 32-bit buffer offsets
   if (N * s->d * esz > (int64_t)INT32_MAX || NB * s->d * 64 * esz > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
   const int64_t BH = (int64_t)s->B * s->H;
-  if (BH > 65535 || BH * NB > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  // launch limits: the grid of one launch holds at most 2^32 - 1 work-items per
+  // dimension, and the largest grids are the predictor's pooling (2 x 256
+  // work-items per (b, h, tile)) and the attention kernels (256 per tile)
+  if (BH > 65535 || BH * NB * 512 > (int64_t)UINT32_MAX) return DSA_ERR_SHAPE;
   Geo g;
   g.Lt = s->Lt; g.Lh = s->Lh; g.Lw = s->Lw;
   g.tt = s->tt; g.th = s->th; g.tw = s->tw;
@@ -61,7 +64,7 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t dvec, bitmap, counts, offsets, entries, do16, dmax, dscale, total;
+  size_t dvec, bitmap, counts, offsets, entries, do16, dmax, dscale, vmax, vscale, total;
   int words;
 };
 
@@ -78,9 +81,19 @@ BwdLayout bwd_layout(const Derived& dv, int kmax) {
   l.do16 = off;    off += dv.io_f32 ? 0 : align256(BH * N * (size_t)dv.d * 2);
   l.dmax = off;    off += dv.io_f32 ? 0 : align256(BH * kDoChunks * sizeof(uint32_t));
   l.dscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
+  l.vmax = off;    off += dv.io_f32 ? 0 : align256(BH * kDoChunks * sizeof(uint32_t));
+  l.vscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
   l.total = off;
   return l;
 }
+
+// The reverse index stores, per head, offsets into a list of at most NB * kmax
+// entries as int32: larger selections are rejected.
+bool csc_fits(const Derived& dv, int kmax) { return (int64_t)dv.g.NB * kmax <= (int64_t)INT32_MAX; }
+
+// softmax scale: finite and positive (the kernels take the row maximum of the
+// unscaled scores)
+bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
 }  // namespace
 
@@ -102,7 +115,7 @@ const char* dsa_status_string(dsa_status s) {
   return "unknown dsa_status";
 }
 
-int32_t dsa_version(void) { return 100; }
+int32_t dsa_version(void) { return 200; }
 
 dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q, const void* K, const void* Wq,
                        const void* Wk, float* Qbar, float* Kbar, float* S, hipStream_t stream) {
@@ -221,7 +234,7 @@ dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, co
   if (st != DSA_OK) return st;
   if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
   if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
-  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  if (!scale_ok(scale)) return DSA_ERR_SHAPE;
   if (dv.BH == 0) return DSA_OK;
   if (!Q || !K || !V || !idx || !k || !O || !LSE) return DSA_ERR_NULL;
   const size_t need = attn_fwd_workspace_bytes(dv.BH, dv.g.NB, dv.d, dv.io_f32);
@@ -238,7 +251,7 @@ dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, co
 size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax) {
   Derived dv;
   if (derive(shape, &dv) != DSA_OK) return 0;
-  if (kmax < 1 || kmax > dv.g.NB) return 0;
+  if (kmax < 1 || kmax > dv.g.NB || !csc_fits(dv, kmax)) return 0;
   return bwd_layout(dv, kmax).total;
 }
 
@@ -255,9 +268,12 @@ dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const v
   dsa_status st = derive(shape, &dv);
   if (st != DSA_OK) return st;
   if ((phases & (kDkdv | kDq)) && out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  if ((phases & kPrepare) && o_dtype != DSA_F32 && o_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
-  if ((phases & (kDkdv | kDq)) && !isfinite(scale)) return DSA_ERR_SHAPE;
+  // O enters the backward only through D = rowsum(dO * O); a rounded O puts a
+  // coherent error into every dS of its row, so only the float32 forward output
+  // is accepted
+  if ((phases & kPrepare) && o_dtype != DSA_F32) return DSA_ERR_DTYPE;
+  if (kmax < 1 || kmax > dv.g.NB || !csc_fits(dv, kmax)) return DSA_ERR_K;
+  if ((phases & (kDkdv | kDq)) && !scale_ok(scale)) return DSA_ERR_SHAPE;
   if (dv.BH == 0) return DSA_OK;
   if ((phases & kPrepare) && (!O || !dO || !idx || !k)) return DSA_ERR_NULL;
   if ((phases & kDkdv) && (!Q || !K || !V || !dO || !LSE || !dK || !dV)) return DSA_ERR_NULL;
@@ -266,7 +282,7 @@ dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const v
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255u)) return DSA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   BwdArgs a;
-  a.Q = Q; a.K = K; a.V = V; a.O = O; a.o_f32 = o_dtype == DSA_F32; a.dO = dO; a.LSE = LSE;
+  a.Q = Q; a.K = K; a.V = V; a.O = static_cast<const float*>(O); a.dO = dO; a.LSE = LSE;
   a.idx = idx; a.kvec = k; a.kmax = kmax;
   a.scale = scale; a.c = scale * kLog2e; a.out_f32 = out_dtype == DSA_F32;
   a.dQ = dQ; a.dK = dK; a.dV = dV;
@@ -278,6 +294,8 @@ dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const v
   a.dO16 = dv.io_f32 ? nullptr : ws + l.do16;
   a.dmax = dv.io_f32 ? nullptr : reinterpret_cast<uint32_t*>(ws + l.dmax);
   a.dscale = dv.io_f32 ? nullptr : reinterpret_cast<float2*>(ws + l.dscale);
+  a.vmax = dv.io_f32 ? nullptr : reinterpret_cast<uint32_t*>(ws + l.vmax);
+  a.vscale = dv.io_f32 ? nullptr : reinterpret_cast<float2*>(ws + l.vscale);
   a.words = l.words;
   a.g = dv.g; a.BH = dv.BH;
   hipError_t e = hipSuccess;

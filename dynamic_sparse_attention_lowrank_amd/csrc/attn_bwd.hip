@@ -37,89 +37,46 @@ namespace dsa {
 namespace {
 
 // ---------------------------------------------------------------- 1. scale of the fp16 dO copy
-// fp16 keeps 11 significant bits but only 5 exponent bits: a plain conversion
-// drops bits of every bf16 gradient below 2^-17 in magnitude and turns those
-// below 2^-25 into zero, the usual size of training gradients.  The copy holds
-// dO * 2^s instead, one power of two per (b, h), chosen so that the head's
-// largest |dO| lands in [2^14, 2^15): every element within a factor 2^31 of it
-// converts exactly, and the products are brought back by 2^-s in fp32, exactly.
-// (a) per-chunk maxima of the magnitude bits: for finite bf16 values the integer
-//     order of (bits & 0x7fff) is the order of |x|, and a maximum is order-free.
-__global__ __launch_bounds__(256) void do_absmax_kernel(BwdArgs a, int D) {
-  const int bh = blockIdx.x / kDoChunks, c = blockIdx.x - bh * kDoChunks;
-  const size_t n16 = (size_t)a.g.N * D / 8;   // 16-byte chunks (8 bf16) per head
-  const u32x4* __restrict__ p = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(a.dO) + (size_t)bh * a.g.N * D);
-  uint32_t m = 0;
-  for (size_t i = (size_t)c * 256 + threadIdx.x; i < n16; i += (size_t)kDoChunks * 256) {
-    const u32x4 v = p[i];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m = max(m, max(v[e] & 0x7fffu, (v[e] >> 16) & 0x7fffu));
-  }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
-  __shared__ uint32_t wm[4];
-  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) a.dmax[blockIdx.x] = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
-}
-// (b) one wave per (b, h): s = 14 - floor(log2 max|dO|), clamped to [-64, 64]
-//     (2^s and 2^-s stay normal floats); s = 0 for an all-zero or non-finite dO.
-static_assert(kDoChunks == 64, "one lane per chunk");
-__global__ __launch_bounds__(64) void do_scale_kernel(BwdArgs a) {
-  const int bh = blockIdx.x;
-  uint32_t m = a.dmax[(size_t)bh * kDoChunks + threadIdx.x];
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
-  if (threadIdx.x == 0) {
-    int s = 0;
-    if (m != 0u && m < 0x7f80u) {
-      const int e = (int)(m >> 7);            // biased exponent (0: subnormal, below 2^-126)
-      s = e == 0 ? 64 : 14 - (e - 127);
-      s = s < -64 ? -64 : (s > 64 ? 64 : s);
-    }
-    a.dscale[bh] = make_float2(__uint_as_float((uint32_t)(127 + s) << 23), __uint_as_float((uint32_t)(127 - s) << 23));
-  }
-}
+// dO and V enter fp16 products (dV = P^T dO, dP = dO V^T): each is converted
+// after multiplying it by its own power of two per (b, h) (launch_pow2_scale), so
+// the conversion is exact whatever the size of the values, and dP and dV are
+// multiplied back by the inverse powers in fp32, exactly.
 
 // ---------------------------------------------------------------- 2. D = rowsum(dO * O)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   constexpr int CE = Elem<T>::kChunkElems;
   constexpr int CPR = D / CE;                 // lanes per token
-  constexpr int TPB = 256 / CPR;              // tokens per work-group
+  constexpr int TPB = 256 / CPR;              // tokens per work-group and trip
   const size_t total = (size_t)a.BH * a.g.N;
-  const size_t tok = (size_t)blockIdx.x * TPB + threadIdx.x / CPR;
   const int c = threadIdx.x % CPR;
-  float s = 0.f;
-  if (tok < total) {
-    const u32x4 g = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.dO) + tok * D + c * CE);
-    const T* gv = reinterpret_cast<const T*>(&g);
-    float ov[CE];
-    if (a.o_f32) {
-      const float* O = reinterpret_cast<const float*>(a.O) + tok * D + c * CE;
+  for (size_t t0 = (size_t)blockIdx.x * TPB; t0 < total; t0 += (size_t)gridDim.x * TPB) {
+    const size_t tok = t0 + threadIdx.x / CPR;
+    float s = 0.f;
+    if (tok < total) {
+      const u32x4 g = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.dO) + tok * D + c * CE);
+      const T* gv = reinterpret_cast<const T*>(&g);
+      const float* O = a.O + tok * D + c * CE;
+      float ov[CE];
 #pragma unroll
       for (int q = 0; q < CE / 4; ++q) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(O + 4 * q);
         ov[4 * q] = v[0]; ov[4 * q + 1] = v[1]; ov[4 * q + 2] = v[2]; ov[4 * q + 3] = v[3];
       }
-    } else {
-      const bf16* O = reinterpret_cast<const bf16*>(a.O) + tok * D + c * CE;
 #pragma unroll
-      for (int e = 0; e < CE; ++e) ov[e] = (float)O[e];
+      for (int e = 0; e < CE; ++e) s = fmaf(ov[e], to_f32(gv[e]), s);
+      if constexpr (sizeof(T) == 2) {            // scaled fp16 copy of dO for the fp16 products
+        const float up = a.dscale[tok / a.g.N].x;
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) h[e] = (f16)(to_f32(gv[e]) * up);
+        *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.dO16) + tok * D + c * CE) = h;
+      }
     }
 #pragma unroll
-    for (int e = 0; e < CE; ++e) s = fmaf(ov[e], to_f32(gv[e]), s);
-    if constexpr (sizeof(T) == 2) {            // scaled fp16 copy of dO for the fp16 products
-      const float up = a.dscale[tok / a.g.N].x;
-      f16x8 h;
-#pragma unroll
-      for (int e = 0; e < CE; ++e) h[e] = (f16)(to_f32(gv[e]) * up);
-      *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.dO16) + tok * D + c * CE) = h;
-    }
+    for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (tok < total && c == 0) a.Dvec[tok] = s;
   }
-#pragma unroll
-  for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-  if (tok < total && c == 0) a.Dvec[tok] = s;
 }
 
 // ---------------------------------------------------------------- 3. reverse index
@@ -128,19 +85,20 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ 
 }
 
 __global__ __launch_bounds__(256) void rev_setbits_kernel(BwdArgs a) {
-  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
   const int NB = a.g.NB;
-  if (id >= (size_t)a.BH * NB * a.kmax) return;
-  const int slot = (int)(id % a.kmax);
-  const size_t row = id / a.kmax;             // bh * NB + tau
-  const int bh = (int)(row / NB);
-  const int tau = (int)(row % NB);
-  int kk = a.kvec[bh];
-  kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
-  if (slot >= kk) return;
-  const int j = a.idx[id];
-  if ((unsigned)j >= (unsigned)NB) return;
-  atomicOr(&a.bitmap[((size_t)bh * NB + j) * a.words + (tau >> 5)], 1u << (tau & 31));
+  const size_t n = (size_t)a.BH * NB * a.kmax;
+  for (size_t id = (size_t)blockIdx.x * 256 + threadIdx.x; id < n; id += (size_t)gridDim.x * 256) {
+    const int slot = (int)(id % a.kmax);
+    const size_t row = id / a.kmax;             // bh * NB + tau
+    const int bh = (int)(row / NB);
+    const int tau = (int)(row % NB);
+    int kk = a.kvec[bh];
+    kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
+    if (slot >= kk) continue;
+    const int j = a.idx[id];
+    if ((unsigned)j >= (unsigned)NB) continue;
+    atomicOr(&a.bitmap[((size_t)bh * NB + j) * a.words + (tau >> 5)], 1u << (tau & 31));
+  }
 }
 
 // one wave per (head, key block)
@@ -230,13 +188,13 @@ template <typename T> struct GradType;
 template <> struct GradType<bf16> { typedef f16 type; };
 template <> struct GradType<float> { typedef float type; };
 
-__device__ __forceinline__ f16x8 to_grad_frag(bf16x8 v, f16*) {
+__device__ __forceinline__ f16x8 to_grad_frag(bf16x8 v, float up, f16*) {
   f16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (f16)(float)v[e];
+  for (int e = 0; e < 8; ++e) r[e] = (f16)((float)v[e] * up);
   return r;
 }
-__device__ __forceinline__ f32x8 to_grad_frag(f32x8 v, float*) { return v; }
+__device__ __forceinline__ f32x8 to_grad_frag(f32x8 v, float, float*) { return v; }
 
 // One work-group of 4 waves per key block, two waves per SIMD (<= 256 registers);
 // wave w owns keys 16w..16w+15, whose K and V rows stay in registers as the B
@@ -286,12 +244,20 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int k_tok = jbase + (k_ok ? member_offset(g, kr) : 0);
   Frag kf[KS];
   GFrag vf[KS];
+  float dinv = 1.f, dpinv = 1.f;              // 2^-s of the fp16 dO copy; 2^-(s+t) for dP
   load_row_frags16<T, D>(kf, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, q);
   {
     Frag vt[KS];
     load_row_frags16<T, D>(vt, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, q);
+    float vup = 1.f;
+    if constexpr (sizeof(T) == 2) {
+      const float2 vs = a.vscale[bh];
+      vup = vs.x;
+      dinv = a.dscale[bh].y;
+      dpinv = dinv * vs.y;                    // both in [2^-63, 2^63]: exact, normal
+    }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) vf[s] = to_grad_frag(vt[s], (G*)nullptr);
+    for (int s = 0; s < KS; ++s) vf[s] = to_grad_frag(vt[s], vup, (G*)nullptr);
   }
 
   int qoff[DmaCfg<T, D, W>::kPer], goff[DmaCfg<G, D, W>::kPer];
@@ -306,8 +272,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dv[t] = f32x4{};
   }
   const float c2 = a.c;
-  float dinv = 1.f;                           // 2^-s of the fp16 dO copy
-  if constexpr (sizeof(T) == 2) dinv = a.dscale[bh].y;
   const int* list = a.entries + (size_t)bh * g.NB * a.kmax;
   const int* off = a.offsets + (size_t)bh * (g.NB + 1);
   const int e0 = off[j], n = off[j + 1] - e0;
@@ -392,7 +356,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
           float p = fast_exp2(fmaf(sacc[mt][i], c2, -l4[i] * kLog2e));
           if constexpr (!FULL) p = (r0 + i < g.T) ? p : 0.f;      // padding query rows
           pv[4 * hf + i] = p;
-          sv[4 * hf + i] = p * fmaf(pacc[mt][i], dinv, -d4[i]);
+          sv[4 * hf + i] = p * fmaf(pacc[mt][i], dpinv, -d4[i]);
         }
       }
       pf[ks] = to_frag(pv, (G*)nullptr);
@@ -681,15 +645,18 @@ hipError_t launch_prepare_t(const BwdArgs& a, hipStream_t s) {
   const size_t tokens = (size_t)a.BH * a.g.N;
   const int tpb = 256 / CPR;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL(do_absmax_kernel, dim3((unsigned)(a.BH * kDoChunks)), dim3(256), 0, s, a, D);
-    hipLaunchKernelGGL(do_scale_kernel, dim3((unsigned)a.BH), dim3(64), 0, s, a);
+    const hipError_t e = launch_pow2_scale(a.dO, a.BH, (size_t)a.g.N * D, a.dmax, a.dscale, s);
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((tokens + tpb - 1) / tpb)), dim3(256), 0, s, a);
+  const size_t pgrid = (tokens + tpb - 1) / tpb;
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)(pgrid < (1u << 20) ? pgrid : (1u << 20))), dim3(256), 0,
+                     s, a);
   const size_t nwords = (size_t)a.BH * a.g.NB * a.words;
   const unsigned zgrid = (unsigned)((nwords + 255) / 256 < 65536 ? (nwords + 255) / 256 : 65536);
   hipLaunchKernelGGL(zero_words_kernel, dim3(zgrid), dim3(256), 0, s, a.bitmap, nwords);
   const size_t nslots = (size_t)a.BH * a.g.NB * a.kmax;
-  hipLaunchKernelGGL(rev_setbits_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, a);
+  const size_t sgrid = (nslots + 255) / 256;
+  hipLaunchKernelGGL(rev_setbits_kernel, dim3((unsigned)(sgrid < (1u << 20) ? sgrid : (1u << 20))), dim3(256), 0, s, a);
   const unsigned rows4 = (unsigned)(((size_t)a.BH * a.g.NB + 3) / 4);
   hipLaunchKernelGGL(rev_count_kernel, dim3(rows4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(rev_scan_kernel, dim3(a.BH), dim3(1024), 0, s, a);
@@ -706,6 +673,9 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, int io_f32, int d, hipStream_t s
 
 template <typename T, int D>
 void launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (launch_pow2_scale(a.V, a.BH, (size_t)a.g.N * D, a.vmax, a.vscale, s) != hipSuccess) return;
+  }
   const dim3 grid(a.BH * a.g.NB), block(256);
   if (a.g.T == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, block, 0, s, a);

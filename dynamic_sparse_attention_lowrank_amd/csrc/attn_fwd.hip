@@ -25,11 +25,14 @@
 //     K(j+1) is requested as soon as S(j) has consumed K(j), V(j+1) as soon as the
 //     P.V product has consumed V(j).  Each wave keeps its own running max / sum /
 //     O over its key half; the halves are merged once, through LDS, at the end.
-// With bf16 inputs the P.V product runs on fp16 matrix cores (V converted in
-// kv_prep, exact for |v| < 65504; P rounded to fp16, 2^-12 relative) and the row
-// sum adds the same fp16 probabilities (v_dot2, fp32 accumulation).  The running
-// maximum only moves when a row's maximum grows by more than 2^8, so most blocks
-// skip rescaling O; this is exact (numerator and denominator share the maximum).
+// With bf16 inputs the P.V product runs on fp16 matrix cores: kv_prep converts
+// V * 2^t, with one power of two per (b, h) that puts the head's largest |v| in
+// [2^14, 2^15) (launch_pow2_scale), so the conversion is exact whatever the size
+// of V, and the output is multiplied by 2^-t in fp32, exactly; P is rounded to
+// fp16 (2^-12 relative) and the row sum adds the same fp16 probabilities (v_dot2,
+// fp32 accumulation).  The running maximum only moves when a row's maximum grows
+// by more than 2^8, so most blocks skip rescaling O; this is exact (numerator and
+// denominator share the maximum).
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -134,6 +137,7 @@ __global__ __launch_bounds__(256) void kv_prep16_kernel(FwdArgs a) {
   const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + hoff;
   const int base = tile_base(g, j);
   const int tid = threadIdx.x;
+  const float vup = a.vscale[bh].x;                            // 2^t of this head
 #pragma unroll
   for (int i = 0; i < NCH / 256; ++i) {
     const int idx = tid + 256 * i, r = idx / CPR, c = idx % CPR;
@@ -181,8 +185,8 @@ __global__ __launch_bounds__(256) void kv_prep16_kernel(FwdArgs a) {
     PT e[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      e[q] = (PT)(float)x0[q];
-      e[4 + q] = (PT)(float)x1[q];
+      e[q] = (PT)((float)x0[q] * vup);
+      e[4 + q] = (PT)((float)x1[q] * vup);
     }
     vo[o] = *reinterpret_cast<const u32x4*>(e);
   }
@@ -458,7 +462,8 @@ void attn_fwd_kernel(FwdArgs a) {
   const float wa = (ma == -INFINITY) ? 0.f : fast_exp2(ma - mt);
   const float wb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - mt);
   const float l_tot = wa * la + wb * lb;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if constexpr (sizeof(T) == 2) inv *= a.vscale[bh].y;        // undo the fp16 copy's 2^t (exact)
   const int q = 32 * w + l32;
   if (q < g.T) {
     const int q_tok = tau_base + member_offset(g, q);
@@ -484,11 +489,17 @@ void attn_fwd_kernel(FwdArgs a) {
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
   FwdArgs a = a0;
+  const size_t copy = (size_t)a0.BH * a0.g.NB * 64 * D * sizeof(T);   // one fragment-major copy
   a.Kf = a0.Vt;
-  a.Vt = reinterpret_cast<char*>(a0.Vt) + (size_t)a0.BH * a0.g.NB * 64 * D * sizeof(T);
-  if constexpr (sizeof(T) == 2)
+  a.Vt = reinterpret_cast<char*>(a0.Vt) + copy;
+  if constexpr (sizeof(T) == 2) {
+    char* tail = reinterpret_cast<char*>(a0.Vt) + 2 * copy;
+    a.vmax = reinterpret_cast<uint32_t*>(tail);
+    a.vscale = reinterpret_cast<float2*>(tail + (((size_t)a0.BH * kDoChunks * 4 + 255) & ~(size_t)255));
+    const hipError_t e = launch_pow2_scale(a.V, a.BH, (size_t)a.g.N * D, a.vmax, a.vscale, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((kv_prep16_kernel<D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
-  else
+  } else
     hipLaunchKernelGGL((kv_prep_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
   if (a.g.T == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
   else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(a.BH * a.g.NB), dim3(kTileThreads), 0, s, a);
@@ -498,7 +509,10 @@ hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
 }  // namespace
 
 size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32) {
-  return 2 * (size_t)BH * NB * d * 64 * (io_f32 ? 4 : 2);      // K and V^T, fragment-major
+  const size_t copies = 2 * (size_t)BH * NB * d * 64 * (io_f32 ? 4 : 2);      // K and V^T, fragment-major
+  if (io_f32) return copies;
+  // bf16: partial maxima and the power-of-two scale of V, 256-byte aligned sections
+  return copies + (((size_t)BH * kDoChunks * 4 + 255) & ~(size_t)255) + (((size_t)BH * 8 + 255) & ~(size_t)255);
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s) {

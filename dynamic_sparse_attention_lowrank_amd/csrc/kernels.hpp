@@ -24,6 +24,8 @@ struct FwdArgs {
   float c;      // scale * log2(e)
   void* Vt;     // workspace: per block, V transposed to [d][64 key positions]
   void* Kf;     // workspace: per block, K in fragment order (when used)
+  uint32_t* vmax;   // workspace [BH][kDoChunks]: partial max |V| (bf16 inputs)
+  float2* vscale;   // workspace [BH]: (2^t, 2^-t), the fp16 V copy's power-of-two scale
   Geo g;
   int BH;
 };
@@ -104,15 +106,22 @@ hipError_t launch_fused_select(const FusedSelectArgs& a, hipStream_t s);
 // pooled features only (the first half of launch_predict)
 hipError_t launch_pool_project(const PredictArgs& a, int io_f32, int d, hipStream_t s);
 
-// per-(b, h) chunks of the dO magnitude reduction (one wave reduces them)
+// per-(b, h) chunks of the magnitude reductions behind the power-of-two scales
+// (one wave reduces them)
 constexpr int kDoChunks = 64;
+
+// Per-(b, h) power-of-two scale of a bf16 [BH][elems_per_head] tensor (elems_per_head
+// a multiple of 8, rows 16-byte aligned): scale[bh] = (2^s, 2^-s) with s such that
+// the head's largest magnitude times 2^s lies in [2^14, 2^15) (s in [-63, 63]; 0 for
+// an all-zero head).  `partial` holds BH * kDoChunks words.
+hipError_t launch_pow2_scale(const void* X, int BH, size_t elems_per_head, uint32_t* partial, float2* scale,
+                             hipStream_t s);
 
 struct BwdArgs {
   const void* Q;
   const void* K;
   const void* V;
-  const void* O;
-  int o_f32;            // O is float32 (else bf16)
+  const float* O;       // forward output, float32
   const void* dO;
   const float* LSE;
   const int32_t* idx;
@@ -129,6 +138,8 @@ struct BwdArgs {
   void* dO16;           // [BH, N, d] fp16 copy of dO * 2^s_bh (bf16 inputs; written by prepare)
   uint32_t* dmax;       // [BH, kDoChunks] partial max |dO| (bf16 magnitude bits; bf16 inputs)
   float2* dscale;       // [BH] (2^s_bh, 2^-s_bh): the fp16 copy's exact power-of-two scale
+  uint32_t* vmax;       // [BH, kDoChunks] partial max |V| (bf16 inputs; written by the dK/dV phase)
+  float2* vscale;       // [BH] (2^t_bh, 2^-t_bh): scale of V before its fp16 conversion in dK/dV
   uint32_t* bitmap;     // [BH, NB, words]   bit tau of row j: tile tau kept block j
   int32_t* counts;      // [BH, NB]
   int32_t* offsets;     // [BH, NB + 1]

@@ -23,7 +23,8 @@
  *   shape->io (DSA_BF16 or DSA_F32) unless an argument says otherwise.
  * Empty input.  B*H == 0 is valid: the call returns DSA_OK and enqueues nothing.
  * Limits.  N*d*esize and NB*d*64*esize below 2^31 bytes (esize = 2 for bf16, 4 for
- *   fp32), B*H <= 65535, B*H*NB <= 2^31-1 (DSA_ERR_SHAPE).
+ *   fp32), B*H <= 65535, and B*H*NB*512 <= 2^32-1 (the work-items of the largest
+ *   launch grid) (DSA_ERR_SHAPE).
  * Ownership.  The caller owns every buffer and the stream.  The library never
  *   allocates memory, never synchronises the device and keeps no state between
  *   calls; each call only enqueues kernels on `stream` and returns.
@@ -79,7 +80,7 @@ typedef struct {
 /* Human-readable name of a status code (static storage, never NULL). */
 DSA_API const char* dsa_status_string(dsa_status s);
 
-/* Library ABI version (major*10000 + minor*100 + patch). */
+/* Library ABI version (major*100 + minor): 200. */
 DSA_API int32_t dsa_version(void);
 
 /*
@@ -186,9 +187,11 @@ DSA_API dsa_status dsa_rope3d(const dsa_shape* shape, int32_t dtype, float base,
 /*
  * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
  * this shape (0 on invalid arguments): 2*B*H*NB*d*64 elements of 2 bytes (bf16
- * io) or 4 bytes (fp32 io).  dsa_attn_fwd first rewrites every key block's K
- * and V (V transposed; fp16 for bf16 io) there in the order its matrix-core
- * fragments are loaded.
+ * io) or 4 bytes (fp32 io), and for bf16 io two more 256-byte-aligned sections of
+ * B*H*64 words and B*H float pairs.  dsa_attn_fwd first rewrites every key
+ * block's K and V (V transposed; fp16 for bf16 io) there in the order its
+ * matrix-core fragments are loaded, after finding V's power-of-two scale per
+ * (b, h) (the two small sections).
  */
 DSA_API size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape);
 
@@ -200,14 +203,16 @@ DSA_API size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape);
  *   O_i = sum_n softmax_n(s_in) v_n,  LSE_i = ln sum_n exp(s_in).
  *   Q, K, V: [B,H,N,d] io dtype.  idx: [B,H,NB,kmax] int32, k: device int32 [B*H].
  *   out_dtype: element type of O (DSA_BF16 or DSA_F32, any io).  O: [B,H,N,d].
- *   LSE: [B,H,N] float32 (natural log).  scale is normally 1/sqrt(d).
+ *   LSE: [B,H,N] float32 (natural log).  scale must be finite and > 0 (normally
+ *   1/sqrt(d)); otherwise DSA_ERR_SHAPE.
  *   workspace: device memory of at least dsa_attn_fwd_workspace_bytes(shape)
  *   bytes, 256-byte aligned; contents on entry do not matter (DSA_ERR_WORKSPACE).
  *   Softmax statistics and accumulation are float32.  With bf16 io the P.V
- *   product runs on fp16 matrix cores: V is converted to fp16 (a precondition:
- *   exact for 2^-17 <= |v| < 65504; larger magnitudes overflow, smaller ones are
- *   rounded to multiples of 2^-24, an absolute error of at most 2^-25 per
- *   element) and the probabilities are rounded to fp16.
+ *   product runs on fp16 matrix cores: V is multiplied by 2^t, one power of two
+ *   per (b, h) that puts the head's largest |v| in [2^14, 2^15) (t in [-63, 63]),
+ *   and converted to fp16, which is exact for every element within a factor 2^31
+ *   of that maximum whatever the size of V; O is multiplied back by 2^-t in fp32
+ *   (exact).  The probabilities are rounded to fp16 (2^-12 relative).
  *   Device-side robustness: k is clamped to [1, kmax]; idx entries outside
  *   [0, NB) are skipped; a row with no valid block gets O = 0, LSE = -inf.
  *   Duplicate entries are the caller's responsibility (dsa_select never makes them).
@@ -219,33 +224,41 @@ DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const voi
 
 /*
  * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for
- * this shape and kmax (0 on invalid arguments).  It holds D = rowsum(dO * O),
- * the reverse (key block -> query tiles) index of idx and, for bf16 inputs, an
- * fp16 copy of dO (B*H*N*d*2 bytes) for the fp16 products of the backward with
- * its per-(b, h) scale (B*H*64 partial maxima and B*H float pairs).
+ * this shape and kmax (0 on invalid arguments, including NB*kmax > 2^31-1: the
+ * reverse index keeps 32-bit offsets per head).  It holds D = rowsum(dO * O),
+ * the reverse (key block -> query tiles) index of idx (for every key block, the
+ * query tiles whose kept set contains it: the sums over queries of dK and dV in
+ * the DSV page's stage two, section 4, run over these lists) and, for bf16
+ * inputs, an fp16 copy of dO (B*H*N*d*2 bytes) for the fp16 products of the
+ * backward, with the per-(b, h) scales of dO and of V (for each, B*H*64 partial
+ * maxima and B*H float pairs).  Sections are 256-byte aligned.
  */
 DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
 
 /*
  * dsa_attn_bwd -- gradients of the block-sparse attention with the block mask
- * held fixed (no gradient reaches the predictor).
+ * held fixed (no gradient reaches the predictor).  The DSV page trains the video
+ * DiT through its sparse attention in stage two (section 4), so the kept blocks
+ * need exact gradients:
  *   D_i = dO_i . O_i,  P from the forward's LSE,  dS_in = P_in (dO_i . v_n - D_i),
  *   dQ_i = scale sum_n dS_in k_n,  dK_n = scale sum_i dS_in q_i,  dV_n = sum_i P_in dO_i.
  *   Q, K, V, dO: [B,H,N,d] io dtype; LSE: [B,H,N] float32 from dsa_attn_fwd.
- *   O: [B,H,N,d] forward output of element type o_dtype (DSA_F32 or DSA_BF16).
- *   O only enters through D; its rounding enters D coherently over a whole row,
- *   so pass the float32 forward output when gradients must match to ~1e-3.
- *   idx, k, kmax, scale: as passed to dsa_attn_fwd.
+ *   O: [B,H,N,d] float32 forward output; o_dtype must be DSA_F32 (else
+ *   DSA_ERR_DTYPE): O only enters through D, where a rounded O would put one
+ *   coherent error into every dS of its row.
+ *   idx, k, kmax, scale: as passed to dsa_attn_fwd (scale finite and > 0; NB*kmax
+ *   <= 2^31-1, else DSA_ERR_K).
  *   dQ, dK, dV: outputs [B,H,N,d] of out_dtype, fully overwritten.
  *   workspace: device memory of at least dsa_attn_bwd_workspace_bytes(shape, kmax)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
  *   Precision with bf16 inputs: dV = P^T dO and dP = dO V^T run on fp16 matrix
- *   cores (P in [0,1] rounded to fp16; dO converted to fp16 after multiplying it
- *   by 2^s, one power of two per (b, h) that puts the head's largest |dO| in
- *   [2^14, 2^15), so the conversion is exact for every element within a factor
- *   2^31 of that maximum, whatever the size of the gradients; the products are
- *   scaled back by 2^-s in fp32, exactly); products with dS use a bf16 hi+lo pair
- *   (two matrix-core passes), so their accuracy does not depend on the scale of dS.
+ *   cores (P in [0,1] rounded to fp16; dO and V converted to fp16 after
+ *   multiplying each by its own power of two per (b, h) that puts the head's
+ *   largest magnitude in [2^14, 2^15), so the conversions are exact for every
+ *   element within a factor 2^31 of that maximum, whatever the size of the
+ *   gradients and values; the products are scaled back in fp32, exactly);
+ *   products with dS use a bf16 hi+lo pair (two matrix-core passes), so their
+ *   accuracy does not depend on the scale of dS.
  *   The same device-side robustness rules as dsa_attn_fwd apply.
  */
 DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V,
@@ -265,7 +278,7 @@ DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const voi
  * dsa_attn_bwd_prepare -- D = rowsum(dO * O) and the reverse index (for every
  *   key block, the ascending list of query tiles that kept it) into the workspace.
  * dsa_attn_bwd_dkdv    -- dK, dV: one pass per key block over the query tiles
- *   that kept it.
+ *   that kept it (it first finds V's power-of-two scale into the workspace).
  * dsa_attn_bwd_dq      -- dQ: one pass per query tile over its kept blocks.
  */
 DSA_API dsa_status dsa_attn_bwd_prepare(const dsa_shape* shape, const void* O, int32_t o_dtype, const void* dO,

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(L):
     raw = ctypes.CDLL(L.library_path)
     for name in declared_functions():
         assert hasattr(raw, name), f"{name} not exported"
-    assert L.lib.dsa_version() == 100
+    assert L.lib.dsa_version() == 200
 
 
 def _shape(L, **kw):
@@ -100,6 +100,11 @@ def test_entry_point_validation(L):
     assert rp(None, 1, 1e4, (0, 0, 0), 0, FAKE, FAKE) == 1
     fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
     assert fneed == 2 * (1 * 2 * 16 * 64 * 64 * 4)                              # K and V^T: 2*B*H*NB*d*64 fp32
+    sh16 = _shape(L, io=1)
+    rnd16 = lambda x: (x + 255) // 256 * 256
+    # bf16: K and V^T copies (2 bytes), then 64 partial maxima and one scale pair of V per (b, h)
+    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh16)) == (2 * (2 * 16 * 64 * 64 * 2) + rnd16(2 * 64 * 4)
+                                                                    + rnd16(2 * 8))
     fw = [FAKE, fneed, None]
     assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, *fw) == 5
     assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, float("nan"), 0, FAKE, FAKE,
@@ -117,8 +122,35 @@ def test_entry_point_validation(L):
     assert lib.dsa_attn_bwd(*args, ctypes.c_void_p(0x1010), need, None) == 6    # misaligned
     bad_o = [ctypes.byref(sh)] + [FAKE] * 4 + [2] + [FAKE] * 4 + [4, 0.125, 0, FAKE, FAKE, FAKE]
     assert lib.dsa_attn_bwd(*bad_o, FAKE, need, None) == 5                      # unknown O dtype
+    bf16_o = [ctypes.byref(sh)] + [FAKE] * 4 + [1] + [FAKE] * 4 + [4, 0.125, 0, FAKE, FAKE, FAKE]
+    assert lib.dsa_attn_bwd(*bf16_o, FAKE, need, None) == 5                     # O must be the fp32 output
+    assert lib.dsa_attn_bwd_prepare(ctypes.byref(sh), FAKE, 1, FAKE, FAKE, FAKE, 4, FAKE, need, None) == 5
+    for bad_scale in (0.0, -0.125, float("inf"), float("nan")):
+        args_s = [ctypes.byref(sh)] + [FAKE] * 4 + [0] + [FAKE] * 4 + [4, bad_scale, 0, FAKE, FAKE, FAKE]
+        assert lib.dsa_attn_bwd(*args_s, FAKE, need, None) == 2
+        assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, bad_scale, 0, FAKE, FAKE,
+                                *fw) == 2
     assert lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 0) == 0
     assert lib.dsa_attn_bwd_workspace_bytes(None, 4) == 0
+
+
+def test_reverse_index_and_launch_limits(L):
+    """Shapes whose per-head reverse index (NB * kmax entries, int32 offsets) or
+    whose launch grids (2^32 - 1 work-items) would overflow are rejected on the host."""
+    lib = L.lib
+    # 65,536 single-token tiles per head: NB * kmax = 65,536 * 32,768 = 2^31 entries
+    sh = _shape(L, B=1, H=1, d=64, Lt=1, Lh=256, Lw=256, tt=1, th=1, tw=1, io=1)
+    assert lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 32768) == 0
+    assert lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 32767) > 0        # 2^31 - 65,536 entries: fits
+    args = [ctypes.byref(sh)] + [FAKE] * 4 + [0] + [FAKE] * 4 + [32768, 0.125, 0, FAKE, FAKE, FAKE]
+    assert lib.dsa_attn_bwd(*args, FAKE, 1 << 40, None) == 4
+    assert lib.dsa_attn_bwd_prepare(ctypes.byref(sh), FAKE, 0, FAKE, FAKE, FAKE, 32768, FAKE, 1 << 40, None) == 4
+    # B*H*NB*512 work-items of the pooling launch: 127 heads fit, 128 do not
+    ok = _shape(L, B=1, H=127, d=64, Lt=1, Lh=256, Lw=256, tt=1, th=1, tw=1, io=1)
+    big = _shape(L, B=1, H=128, d=64, Lt=1, Lh=256, Lw=256, tt=1, th=1, tw=1, io=1)
+    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(ok)) > 0
+    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(big)) == 0
+    assert lib.dsa_predict(ctypes.byref(big), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
 
 
 def test_empty_batch_is_a_no_op(L):
@@ -132,13 +164,13 @@ def test_empty_batch_is_a_no_op(L):
 
 def test_workspace_formula(L):
     """D (fp32 per token) + bitmap (NB x ceil(NB/32) words) + counts + offsets + entries
-    (+ for bf16 inputs an fp16 copy of dO, 64 partial maxima and one scale pair per
-    (b, h)), each section rounded up to 256 bytes."""
+    (+ for bf16 inputs an fp16 copy of dO, and for dO and for V 64 partial maxima and
+    one scale pair per (b, h)), each section rounded up to 256 bytes."""
     sh = _shape(L, B=2, H=3, d=128, Lt=3, Lh=16, Lw=24, tt=1, th=8, tw=8, io=1)
     BH, N, NB, kmax = 6, 3 * 16 * 24, 18, 5
     r = lambda x: (x + 255) // 256 * 256
     want = r(BH * N * 4) + r(BH * NB * 1 * 4) + r(BH * NB * 4) + r(BH * (NB + 1) * 4) + r(BH * NB * kmax * 4)
-    bf16_extra = r(BH * N * 128 * 2) + r(BH * 64 * 4) + r(BH * 2 * 4)   # fp16 dO, its scale
+    bf16_extra = r(BH * N * 128 * 2) + 2 * (r(BH * 64 * 4) + r(BH * 2 * 4))   # fp16 dO; scales of dO and V
     assert L.lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax) == want + bf16_extra
     sh32 = _shape(L, B=2, H=3, d=128, Lt=3, Lh=16, Lw=24, tt=1, th=8, tw=8, io=0)
     assert L.lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh32), kmax) == want

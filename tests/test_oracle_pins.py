@@ -517,3 +517,42 @@ def test_keep_all_gradients_equal_dense_autograd(tiny):
     (out * torch.from_numpy(dO)).sum().backward()
     for mine, ref in ((dQ, q.grad), (dK, k.grad), (dV, v.grad)):
         assert np.abs(mine - ref.numpy()).max() < 1e-11
+
+
+def test_whole_tensor_helpers_follow_batch_major_heads():
+    """The [B, H, ...] helpers must hand head (b, h) its own tensors, its own
+    weights Wq[h], Wk[h] and its own k = k[b*H + h] (b-major).  Every (b, h)
+    below has different data and a different k, so a swapped b/h index, a k taken
+    h-major, or weights taken per b would change some head's result; each head
+    is compared with the pinned per-head functions called on hand-picked slices."""
+    geom = Geometry(2, 4, 4, 1, 2, 2)                  # 32 tokens, 8 blocks of 4
+    mem = geom.members()
+    B, H, d, r = 2, 3, 8, 4
+    rng = np.random.default_rng(11)
+    Q, K, V, dO = (rng.standard_normal((B, H, geom.N, d)) for _ in range(4))
+    Wq, Wk = rng.standard_normal((H, d, r)), rng.standard_normal((H, d, r))
+    k = np.array([1, 3, 5, 8, 2, 6], dtype=np.int32)   # k[b*H + h]: all different
+    kmax = int(k.max())
+    scale = 1 / math.sqrt(d)
+    Qb, Kb, S = oracle.predict(Q, K, Wq, Wk, geom)
+    idx = oracle.select(S, k, kmax)
+    O, LSE = oracle.attn_fwd(Q, K, V, idx, k, geom, scale)
+    dQ, dK, dV = oracle.attn_bwd(Q, K, V, dO, idx, k, geom, scale)
+    for b in range(B):
+        for h in range(H):
+            kk = int(k[b * H + h])
+            qb, kb, s = oracle.predict_head(Q[b, h], K[b, h], Wq[h], Wk[h], mem)
+            assert np.array_equal(Qb[b, h], qb) and np.array_equal(Kb[b, h], kb) and np.array_equal(S[b, h], s)
+            ih = oracle.select_head(s, kk, kmax)
+            assert np.array_equal(idx[b, h], ih)
+            assert (idx[b, h, :, kk:] == -1).all() and (idx[b, h, :, :kk] >= 0).all()
+            o, lse = oracle.attn_fwd_head(Q[b, h], K[b, h], V[b, h], mem, ih, kk, scale)
+            assert np.array_equal(O[b, h], o) and np.array_equal(LSE[b, h], lse)
+            g = oracle.attn_bwd_head(Q[b, h], K[b, h], V[b, h], dO[b, h], mem, ih, kk, scale)
+            for got, want in zip((dQ[b, h], dK[b, h], dV[b, h]), g):
+                assert np.array_equal(got, want)
+    # k = NB for head (1, 0): every block kept, so that head is plain dense attention
+    b, h = 1, 0
+    s = Q[b, h] @ K[b, h].T * scale
+    p = np.exp(s - s.max(1, keepdims=True))
+    assert np.allclose(O[b, h], (p / p.sum(1, keepdims=True)) @ V[b, h], rtol=1e-12, atol=1e-12)
