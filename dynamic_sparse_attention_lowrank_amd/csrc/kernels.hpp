@@ -22,8 +22,7 @@ struct FwdArgs {
   float* LSE;
   int out_f32;
   float c;      // scale * log2(e)
-  void* Vt;     // workspace: per block, V transposed to [d][64 key positions]
-  void* Kf;     // workspace: per block, K in fragment order (when used)
+  void* Vt;     // workspace: per block, V^T in fragment-major order
   uint32_t* vmax;   // workspace [BH][kDoChunks]: partial max |V| (bf16 inputs)
   float2* vscale;   // workspace [BH]: (2^t, 2^-t), the fp16 V copy's power-of-two scale
   Geo g;

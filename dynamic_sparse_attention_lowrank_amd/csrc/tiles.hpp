@@ -229,6 +229,17 @@ __device__ __forceinline__ void dma_tile(u32x4* lds, __amdgpu_buffer_rsrc_t rsrc
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + 64 * (w + W * i)), 16,
                                              off[i] * (int)sizeof(T), tile_bytes, 0, 0);
 }
+// A contiguous run of W * PER KB copied as is (e.g. a fragment-major block): wave w
+// issues chunks w, w + W, ..., lane l moving bytes 16l..16l+15 of each 1 KB chunk.
+template <int PER, int W>
+__device__ __forceinline__ void dma_linear(u32x4* lds, __amdgpu_buffer_rsrc_t rsrc, int src_bytes, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = w + W * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + 64 * c), 16,
+                                             lane * 16 + c * 1024, src_bytes, 0, 0);
+  }
+}
 // 64 floats of one tile row each (e.g. LSE): lane l loads the value of member row l
 __device__ __forceinline__ void dma_row_stats(float* lds, __amdgpu_buffer_rsrc_t rsrc, int tile_bytes, int off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, off * 4, tile_bytes, 0, 0);

@@ -186,12 +186,12 @@ DSA_API dsa_status dsa_rope3d(const dsa_shape* shape, int32_t dtype, float base,
 
 /*
  * dsa_attn_fwd_workspace_bytes -- device workspace that dsa_attn_fwd needs for
- * this shape (0 on invalid arguments): 2*B*H*NB*d*64 elements of 2 bytes (bf16
- * io) or 4 bytes (fp32 io), and for bf16 io two more 256-byte-aligned sections of
+ * this shape (0 on invalid arguments): B*H*NB*d*64 elements of 2 bytes (bf16 io)
+ * or 4 bytes (fp32 io), and for bf16 io two more 256-byte-aligned sections of
  * B*H*64 words and B*H float pairs.  dsa_attn_fwd first rewrites every key
- * block's K and V (V transposed; fp16 for bf16 io) there in the order its
- * matrix-core fragments are loaded, after finding V's power-of-two scale per
- * (b, h) (the two small sections).
+ * block's V there, transposed (fp16 for bf16 io), in the order its matrix-core
+ * fragments are loaded, after finding V's power-of-two scale per (b, h) (the two
+ * small sections).
  */
 DSA_API size_t dsa_attn_fwd_workspace_bytes(const dsa_shape* shape);
 

@@ -99,11 +99,11 @@ def test_entry_point_validation(L):
     assert rp(ctypes.byref(sh), 0, 1e4, (0, 0, 0), 0, ctypes.c_void_p(0x1004), FAKE) == 2   # fp32 pairs: 8-byte aligned
     assert rp(None, 1, 1e4, (0, 0, 0), 0, FAKE, FAKE) == 1
     fneed = lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh))
-    assert fneed == 2 * (1 * 2 * 16 * 64 * 64 * 4)                              # K and V^T: 2*B*H*NB*d*64 fp32
+    assert fneed == 1 * 2 * 16 * 64 * 64 * 4                                    # V^T: B*H*NB*d*64 fp32
     sh16 = _shape(L, io=1)
     rnd16 = lambda x: (x + 255) // 256 * 256
-    # bf16: K and V^T copies (2 bytes), then 64 partial maxima and one scale pair of V per (b, h)
-    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh16)) == (2 * (2 * 16 * 64 * 64 * 2) + rnd16(2 * 64 * 4)
+    # bf16: the fp16 V^T copy, then 64 partial maxima and one scale pair of V per (b, h)
+    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(sh16)) == (2 * 16 * 64 * 64 * 2 + rnd16(2 * 64 * 4)
                                                                     + rnd16(2 * 8))
     fw = [FAKE, fneed, None]
     assert lib.dsa_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, *fw) == 5
