@@ -71,6 +71,8 @@ def _load():
     L.dsa_rope3d.argtypes = [sp, i32, f32, i32, i32, i32, i32, vp, vp, vp]
     L.dsa_attn_fwd.restype = ctypes.c_int
     L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+    L.dsa_attn_fwd_noalloc.restype = ctypes.c_int
+    L.dsa_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp]
     L.dsa_attn_fwd_workspace_bytes.restype = sz
     L.dsa_attn_fwd_workspace_bytes.argtypes = [sp]
     L.dsa_attn_bwd_workspace_bytes.restype = sz
@@ -359,6 +361,26 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tenso
     _check(_L().dsa_attn_fwd(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
                              _io_code(O), _ptr(O), _ptr(LSE), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream()))
+    return O, LSE
+
+
+def attn_fwd_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, k: torch.Tensor,
+                     layout: Layout, out: Tuple[torch.Tensor, torch.Tensor], scale: Optional[float] = None):
+    """attn_fwd into the caller's (O, LSE) without any device allocation: the library
+    uses its fixed per-GPU scratch array instead of a workspace (calls that overlap in
+    time on one GPU race on it)."""
+    B, H, N, d = _qkv(layout, Q, K=K, V=V)
+    kmax = _idx(idx, B, H, layout)
+    _kvec(k, B, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O, LSE = out
+    _expect("O", O, Q.shape, _IO)
+    _expect("LSE", LSE, (B, H, N), torch.float32)
+    _dev(Q, K, V, idx, k, O, LSE)
+    sh = _shape(Q, layout)
+    _check(_L().dsa_attn_fwd_noalloc(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(k), kmax, scale,
+                                     _io_code(O), _ptr(O), _ptr(LSE), _stream()))
     return O, LSE
 
 

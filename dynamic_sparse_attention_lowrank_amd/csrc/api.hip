@@ -1,13 +1,16 @@
 // C ABI of libdsa (declared in include/dsa.h): argument checks on the host,
 // shape derivation, workspace carving and kernel launches.  No entry point
-// allocates memory, synchronises the device or keeps state.
+// allocates memory or synchronises the device; the only state is the per-device
+// address of the fixed scratch array of dsa_attn_fwd_noalloc.
 #include <math.h>
 #include <stdint.h>
 
 #include "dsa.h"
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 
 using namespace dsa;
 
@@ -95,6 +98,35 @@ bool csc_fits(const Derived& dv, int kmax) { return (int64_t)dv.g.NB * kmax <= (
 // unscaled scores)
 bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
+// --- fixed scratch of dsa_attn_fwd_noalloc ------------------------------------
+// One array per GPU (each device that loads this code object holds its own copy,
+// at its own address).  In host code `fwd_scratch` only names the symbol: its
+// device address is looked up once per device with hipGetSymbolAddress and kept
+// in g_scratch_addr; kernels receive that address, never the symbol.
+constexpr size_t kFwdScratchBytes = (size_t)144 << 20;
+static __device__ __align__(256) unsigned char fwd_scratch[kFwdScratchBytes];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// device address of the current device's scratch array (looked up on first use)
+hipError_t fwd_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(fwd_scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255u)) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,6 +143,8 @@ const char* dsa_status_string(dsa_status s) {
     case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP launch failed";
     case DSA_ERR_NOT_IMPLEMENTED: return "DSA_ERR_NOT_IMPLEMENTED";
     case DSA_ERR_RANK: return "DSA_ERR_RANK: predictor rank must be in [1, 64]";
+    case DSA_ERR_SCRATCH:
+      return "DSA_ERR_SCRATCH: one head's forward workspace exceeds the 144 MiB scratch of dsa_attn_fwd_noalloc";
   }
   return "unknown dsa_status";
 }
@@ -246,6 +280,49 @@ dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, co
   a.Vt = workspace;
   a.g = dv.g; a.BH = dv.BH;
   return hip_status(launch_attn_fwd(a, dv.io_f32, dv.d, stream));
+}
+
+dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, const void* K, const void* V,
+                                const int32_t* idx, const int32_t* k, int32_t kmax, float scale, int32_t out_dtype,
+                                void* O, float* LSE, hipStream_t stream) {
+  Derived dv;
+  dsa_status st = derive(shape, &dv);
+  if (st != DSA_OK) return st;
+  if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (kmax < 1 || kmax > dv.g.NB) return DSA_ERR_K;
+  if (!scale_ok(scale)) return DSA_ERR_SHAPE;
+  if (dv.BH == 0) return DSA_OK;
+  if (!Q || !K || !V || !idx || !k || !O || !LSE) return DSA_ERR_NULL;
+  if (attn_fwd_workspace_bytes(1, dv.g.NB, dv.d, dv.io_f32) > kFwdScratchBytes) return DSA_ERR_SCRATCH;
+  // heads per group: as many as the scratch holds (every head's computation is
+  // independent of the others', so grouping changes no result)
+  const size_t per_head = (size_t)dv.g.NB * dv.d * 64 * (dv.io_f32 ? 4 : 2);
+  int G = (int)std::min<size_t>((size_t)dv.BH, kFwdScratchBytes / per_head);
+  while (G > 1 && attn_fwd_workspace_bytes(G, dv.g.NB, dv.d, dv.io_f32) > kFwdScratchBytes) --G;
+  void* ws = nullptr;
+  const hipError_t e = fwd_scratch_address(&ws);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  const size_t in_head = (size_t)dv.g.N * dv.d * (dv.io_f32 ? 4 : 2);          // bytes of one head of Q, K, V
+  const size_t out_head = (size_t)dv.g.N * dv.d * (out_dtype == DSA_F32 ? 4 : 2);
+  for (int h0 = 0; h0 < dv.BH; h0 += G) {
+    FwdArgs a;
+    a.Q = static_cast<const char*>(Q) + h0 * in_head;
+    a.K = static_cast<const char*>(K) + h0 * in_head;
+    a.V = static_cast<const char*>(V) + h0 * in_head;
+    a.idx = idx + (size_t)h0 * dv.g.NB * kmax;
+    a.kvec = k + h0;
+    a.kmax = kmax;
+    a.O = static_cast<char*>(O) + h0 * out_head;
+    a.LSE = LSE + (size_t)h0 * dv.g.N;
+    a.out_f32 = out_dtype == DSA_F32;
+    a.c = scale * kLog2e;
+    a.Vt = ws;
+    a.g = dv.g;
+    a.BH = std::min(G, dv.BH - h0);
+    st = hip_status(launch_attn_fwd(a, dv.io_f32, dv.d, stream));
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
 }
 
 size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax) {

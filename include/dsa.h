@@ -27,7 +27,9 @@
  *   launch grid) (DSA_ERR_SHAPE).
  * Ownership.  The caller owns every buffer and the stream.  The library never
  *   allocates memory, never synchronises the device and keeps no state between
- *   calls; each call only enqueues kernels on `stream` and returns.
+ *   calls; each call only enqueues kernels on `stream` and returns.  The one
+ *   exception is dsa_attn_fwd_noalloc: its workspace is a fixed array in device
+ *   memory that the library's code object holds on each GPU it runs on.
  * Errors.  All argument checks happen on the host before any HIP call; a failed
  *   check returns its status and enqueues nothing.  A failed kernel launch
  *   returns DSA_ERR_HIP.  Device-side values (k[], idx[]) cannot be checked by
@@ -65,7 +67,9 @@ typedef enum {
   DSA_ERR_WORKSPACE = 6,       /* workspace too small or misaligned                */
   DSA_ERR_HIP = 7,             /* a HIP launch failed                              */
   DSA_ERR_NOT_IMPLEMENTED = 8, /* combination not supported by this build          */
-  DSA_ERR_RANK = 9             /* predictor rank r out of range                    */
+  DSA_ERR_RANK = 9,            /* predictor rank r out of range                    */
+  DSA_ERR_SCRATCH = 10         /* one head needs more than dsa_attn_fwd_noalloc's
+                                  fixed device scratch                             */
 } dsa_status;
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
@@ -221,6 +225,29 @@ DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const voi
                                 const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
                                 int32_t out_dtype, void* O, float* LSE, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_attn_fwd_noalloc -- dsa_attn_fwd for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc).  Same arguments, semantics, errors and results (bit-
+ *   identical O and LSE) as dsa_attn_fwd, without the workspace: its V^T copy and
+ *   scale sections live in a fixed device array of 144 MiB (150,994,944 bytes),
+ *   one per GPU, held from the first call on that GPU until the process ends.
+ *   Heads are processed in groups that fit it (the kernels of one group, then the
+ *   next, on `stream`); a shape for which one head's workspace
+ *   (dsa_attn_fwd_workspace_bytes with B = H = 1) exceeds the array returns
+ *   DSA_ERR_SCRATCH: at d = 128 that is NB > 9,215 key blocks for bf16 io
+ *   (589,760 tokens in 64-token tiles) and NB > 4,608 for fp32 io (d = 64:
+ *   18,431 and 9,216).  No hipMalloc, hipFree or allocating library routine is
+ *   called; the first call on a GPU looks up the array's device address
+ *   (hipGetSymbolAddress), which can fail with DSA_ERR_HIP.
+ *   Every call on one GPU shares its array: calls that overlap in time on one GPU
+ *   (different streams, or other host threads) race and give undefined results.
+ *   The array's contents on entry do not matter.
+ */
+DSA_API dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, const void* K, const void* V,
+                                        const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
+                                        int32_t out_dtype, void* O, float* LSE, hipStream_t stream);
 
 /*
  * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for

@@ -30,7 +30,7 @@ def test_header_declares_entry_points():
     names = set(declared_functions())
     assert {"dsa_predict", "dsa_select", "dsa_predict_select", "dsa_attn_fwd", "dsa_attn_bwd",
             "dsa_attn_bwd_workspace_bytes", "dsa_status_string", "dsa_version", "dsa_predictor_grad",
-            "dsa_predictor_grad_workspace_bytes", "dsa_rope3d"} <= names
+            "dsa_predictor_grad_workspace_bytes", "dsa_rope3d", "dsa_attn_fwd_noalloc"} <= names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -132,6 +132,36 @@ def test_entry_point_validation(L):
                                 *fw) == 2
     assert lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), 0) == 0
     assert lib.dsa_attn_bwd_workspace_bytes(None, 4) == 0
+
+
+def test_noalloc_forward_host_checks(L):
+    """dsa_attn_fwd_noalloc: the checks of dsa_attn_fwd, and shapes whose single head
+    needs more than the fixed 144 MiB scratch are rejected (DSA_ERR_SCRATCH) before
+    any HIP call."""
+    lib = L.lib
+    sh = _shape(L)
+    na = lib.dsa_attn_fwd_noalloc
+    assert na(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 3, FAKE, FAKE, None) == 5
+    assert na(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.125, 0, FAKE, FAKE, None) == 4
+    assert na(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, float("nan"), 0, FAKE, FAKE, None) == 2
+    assert na(ctypes.byref(sh), FAKE, FAKE, None, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, None) == 1
+    assert na(None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.125, 0, FAKE, FAKE, None) == 1
+    empty = _shape(L, B=0)
+    assert na(ctypes.byref(empty), None, None, None, None, None, 4, 0.125, 0, None, None, None) == 0
+    scratch = 144 << 20
+    # bf16 d = 128: a head's workspace is NB*128*64*2 bytes plus two 256-byte sections
+    for nb_tiles, lat, code in (((96, 96), (1, 768, 768), 10),):             # NB = 9,216
+        big = _shape(L, H=1, d=128, Lt=lat[0], Lh=lat[1], Lw=lat[2], tt=1, th=8, tw=8, io=1)
+        nb = nb_tiles[0] * nb_tiles[1]
+        assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(big)) == nb * 128 * 64 * 2 + 512 > scratch
+        assert na(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0.125, 1, FAKE, FAKE, None) == code
+    fits = _shape(L, H=1, d=128, Lt=5, Lh=8 * 19, Lw=8 * 97, tt=1, th=8, tw=8, io=1)        # NB = 9,215
+    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(fits)) == 9215 * 128 * 64 * 2 + 512 <= scratch
+    # fp32 d = 128: NB = 4,609 exceeds it (4,608 fills it exactly)
+    f32 = _shape(L, H=1, d=128, Lt=11, Lh=8, Lw=8 * 419, tt=1, th=8, tw=8, io=0)
+    assert lib.dsa_attn_fwd_workspace_bytes(ctypes.byref(f32)) == 4609 * 128 * 64 * 4 > scratch
+    assert na(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0.125, 0, FAKE, FAKE, None) == 10
+    assert b"DSA_ERR_SCRATCH" in lib.dsa_status_string(10)
 
 
 def test_reverse_index_and_launch_limits(L):
