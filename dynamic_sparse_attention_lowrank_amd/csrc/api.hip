@@ -67,7 +67,8 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t dvec, bitmap, counts, offsets, entries, do16, dmax, dscale, vmax, vscale, total;
+  size_t dvec, bitmap, counts, offsets, entries, do16, dmax, dscale, vmax, vscale;
+  size_t dabs, dabs_part, du, q16, qmax, qscale, k16, kmaxp, kscale, vmax_q, vscale_q, total;
   int words;
 };
 
@@ -86,6 +87,21 @@ BwdLayout bwd_layout(const Derived& dv, int kmax) {
   l.dscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
   l.vmax = off;    off += dv.io_f32 ? 0 : align256(BH * kDoChunks * sizeof(uint32_t));
   l.vscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
+  // bf16: the single-pass fp16 dS products (max |D|, scaled D, fp16 copies of Q
+  // for dK/dV and of K for dQ, and their scales; V's scale again for dQ)
+  const size_t part = align256(BH * kDoChunks * sizeof(uint32_t)), sc = align256(BH * 2 * sizeof(float));
+  const size_t copy = align256(BH * N * (size_t)dv.d * 2);
+  l.dabs = off;      off += dv.io_f32 ? 0 : align256(BH * sizeof(uint32_t));
+  l.dabs_part = off; off += dv.io_f32 ? 0 : part;
+  l.du = off;        off += dv.io_f32 ? 0 : align256(BH * N * sizeof(float));
+  l.q16 = off;       off += dv.io_f32 ? 0 : copy;
+  l.qmax = off;      off += dv.io_f32 ? 0 : part;
+  l.qscale = off;    off += dv.io_f32 ? 0 : sc;
+  l.k16 = off;       off += dv.io_f32 ? 0 : copy;
+  l.kmaxp = off;     off += dv.io_f32 ? 0 : part;
+  l.kscale = off;    off += dv.io_f32 ? 0 : sc;
+  l.vmax_q = off;    off += dv.io_f32 ? 0 : part;
+  l.vscale_q = off;  off += dv.io_f32 ? 0 : sc;
   l.total = off;
   return l;
 }
@@ -373,6 +389,18 @@ dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const v
   a.dscale = dv.io_f32 ? nullptr : reinterpret_cast<float2*>(ws + l.dscale);
   a.vmax = dv.io_f32 ? nullptr : reinterpret_cast<uint32_t*>(ws + l.vmax);
   a.vscale = dv.io_f32 ? nullptr : reinterpret_cast<float2*>(ws + l.vscale);
+  auto at = [&](size_t o) -> char* { return dv.io_f32 ? nullptr : ws + o; };
+  a.dabs = reinterpret_cast<uint32_t*>(at(l.dabs));
+  a.dabs_part = reinterpret_cast<uint32_t*>(at(l.dabs_part));
+  a.Du = reinterpret_cast<float*>(at(l.du));
+  a.q16 = at(l.q16);
+  a.qmax = reinterpret_cast<uint32_t*>(at(l.qmax));
+  a.qscale = reinterpret_cast<float2*>(at(l.qscale));
+  a.k16 = at(l.k16);
+  a.kmaxp = reinterpret_cast<uint32_t*>(at(l.kmaxp));
+  a.kscale = reinterpret_cast<float2*>(at(l.kscale));
+  a.vmax_q = reinterpret_cast<uint32_t*>(at(l.vmax_q));
+  a.vscale_q = reinterpret_cast<float2*>(at(l.vscale_q));
   a.words = l.words;
   a.g = dv.g; a.BH = dv.BH;
   hipError_t e = hipSuccess;

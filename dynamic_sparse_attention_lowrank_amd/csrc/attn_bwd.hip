@@ -6,18 +6,21 @@
 //   D_i = dO_i . O_i,  dS_in = P_in (dO_i . v_n - D_i),
 //   dQ_i = scale sum_n dS_in k_n,  dK_n = scale sum_i dS_in q_i,  dV_n = sum_i P_in dO_i.
 //
-// Precision: P and dS are computed in fp32 inside the kernels.  dV = P^T dO runs
-// on fp16 matrix cores (P in [0,1] rounded to fp16, dO from an fp16 copy written
-// by the prepare phase and scaled by a power of two per (b, h), so that it is
-// exact whatever the size of the gradients); the products with dS (dK, dQ)
-// take it as a bf16 pair hi + lo (see common.hpp) issued twice, so they keep
-// fp32-level accuracy whatever the scale of dS.  D is taken from O as passed in
-// (fp32 O keeps D accurate; with bf16 O its rounding enters D coherently across a
-// whole row).
+// Precision: P and dS are computed in fp32 inside the kernels.  With bf16 inputs
+// every product runs on fp16 matrix cores with operands that are exact: dO, V, Q
+// and K enter as fp16 copies scaled by a power of two per (b, h) (or, for the
+// operands a work-group keeps in registers, per 64-row block), which converts
+// every bf16 value exactly whatever the size of the tensors (scale.hip), and the
+// products are brought back by the inverse powers in fp32, exactly.  P in [0, 1]
+// is rounded to fp16 (2^-12 relative).  dS is rounded to fp16 after a power of
+// two 2^u per (b, h) chosen from bounds that hold for every element (ds_exponent
+// below), so it neither overflows nor leaves fp16's normal range for any value
+// within 2^-29 of the bound.  fp32 inputs use fp32 throughout.  D is taken from
+// O as passed in (the fp32 forward output).
 //
 // No floating-point atomics, so results are bit-reproducible:
 //   1. prep:     the per-(b, h) scale of the fp16 dO copy, then D (fp32) for
-//                every token and the scaled copy;
+//                every token, the scaled copy, and max |D| per (b, h);
 //   2. reverse index of the block mask: a bitmap row per key block (bit tau set
 //      if tile tau kept it; integer OR is order-free), popcounts, a per-head
 //      exclusive scan, and an ascending compaction into CSC lists;
@@ -41,6 +44,54 @@ namespace {
 // after multiplying it by its own power of two per (b, h) (launch_pow2_scale), so
 // the conversion is exact whatever the size of the values, and dP and dV are
 // multiplied back by the inverse powers in fp32, exactly.
+
+// Exponent u of the fp16 dS (bf16 inputs).  dS = P (dP - D) with P in [0, 1];
+// |dP| <= d max|dO| max|V| < 2^(30 - s - t + log2 d), where 2^s and 2^t are the
+// power-of-two scales of dO and V (they put each maximum below 2^15), and |D| is
+// at most the max |D| the prepare phase measured.  With M the larger of the two
+// exponents |dS| < 2^(M+1), so dS * 2^u with u = 14 - M stays below 2^15.  Scaling
+// dO or V by a power of two moves u the opposite way and leaves the fp16 dS bit
+// for bit unchanged.  A non-finite max |D| gives u = 0.
+__device__ __forceinline__ int ds_exponent(float2 dsc, float2 vsc, uint32_t dabs, int log2d) {
+  const int s = (int)(__float_as_uint(dsc.x) >> 23) - 127;
+  const int t = (int)(__float_as_uint(vsc.x) >> 23) - 127;
+  if (dabs >= 0x7f800000u) return 0;
+  int M = 30 - s - t + log2d;
+  if (dabs != 0u) M = max(M, (int)(dabs >> 23) - 126);    // |D| < 2^(exponent + 1)
+  const int u = 14 - M;
+  return u < -100 ? -100 : (u > 100 ? 100 : u);
+}
+// 2^e as a float, |e| <= 126
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+template <int D> constexpr int kLog2D = D == 64 ? 6 : 7;
+
+// Power-of-two exponent for a 64-row block held in registers (the same rule as
+// launch_pow2_scale: the block's largest magnitude lands in [2^14, 2^15)): `m` is
+// the lane's largest bf16 magnitude pattern (bits & 0x7fff); every wave of the
+// work-group calls this with its own lanes; `red` is 4 words of LDS.
+__device__ __forceinline__ int block_pow2(uint32_t m, uint32_t* red, int w) {
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh, 64));
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  int e = 0;
+  if (m != 0u && m < 0x7f80u) {
+    const int be = (int)(m >> 7);
+    e = be == 0 ? 63 : 14 - (be - 127);
+    e = e < -63 ? -63 : (e > 63 ? 63 : e);
+  }
+  return e;
+}
+__device__ __forceinline__ uint32_t frag_absmax(const bf16x8* f, int n) {
+  uint32_t m = 0;
+  for (int i = 0; i < n; ++i) {
+    const u32x4 v = __builtin_bit_cast(u32x4, f[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, max(v[e] & 0x7fffu, (v[e] >> 16) & 0x7fffu));
+  }
+  return m;
+}
 
 // ---------------------------------------------------------------- 2. D = rowsum(dO * O)
 template <typename T, int D>
@@ -174,12 +225,22 @@ __global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
   }
 }
 
+// Du = D * 2^u per (b, h) for the dK/dV phase (bf16 inputs); grid (blocks, heads)
+template <int D>
+__global__ __launch_bounds__(256) void scale_d_kernel(BwdArgs a) {
+  const int bh = blockIdx.y;
+  const float up = pow2f(ds_exponent(a.dscale[bh], a.vscale[bh], a.dabs[bh], kLog2D<D>));
+  const float* __restrict__ src = a.Dvec + (size_t)bh * a.g.N;
+  float* __restrict__ dst = a.Du + (size_t)bh * a.g.N;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < a.g.N; i += gridDim.x * 256) dst[i] = src[i] * up;
+}
+
 // ---------------------------------------------------------------- 4. dK, dV
-// Operand types: with bf16 inputs the products that take P or dO (dP = dO V^T,
-// dV = P^T dO) run on fp16 matrix cores (dO * 2^s from the fp16 copy written by
-// the prepare phase, V converted when loaded, P in [0,1] rounded to fp16; both
-// products are multiplied by 2^-s in fp32, exactly); S = Q K^T
-// and dK = dS^T Q stay bf16, dS as a hi+lo pair.  fp32 inputs use fp32 throughout.
+// Operand types: with bf16 inputs every product runs on fp16 matrix cores: Q * 2^a
+// from the fp16 copy of this phase, K * 2^b (b per key block) and V * 2^t converted
+// when loaded, dO * 2^s from the prepare phase's copy, P in [0,1] and dS * 2^u
+// rounded to fp16; the powers of two come back out in fp32, exactly.  fp32 inputs
+// use fp32 throughout.
 // two waves per SIMD for 16-bit inputs; the fp32 variants (parity checks only)
 // need more than 256 registers and run at one
 template <typename T> constexpr int kWavesPerSimd = sizeof(T) == 2 ? 2 : 1;
@@ -210,18 +271,18 @@ __device__ __forceinline__ f32x8 to_grad_frag(f32x8 v, float, float*) { return v
 template <typename T, int D, bool FULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<T>, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
-  typedef typename GradType<T>::type G;
+  typedef typename GradType<T>::type G;      // element type of every streamed tile and operand
   constexpr int W = 4;
-  using C = TileCfg<T, D>;
+  constexpr bool kHalf = sizeof(T) == 2;
   using CG = TileCfg<G, D>;
   typedef typename Elem<T>::frag Frag;
   typedef typename Elem<G>::frag GFrag;
-  typedef typename SplitOf<T>::type Split;
   constexpr int KS = D / 32;                  // 32-wide reduction steps over d
   constexpr int DT = D / 16;                  // 16-wide output tiles over d
-  __shared__ u32x4 q0[C::kRowChunks], q1[C::kRowChunks];
+  __shared__ u32x4 q0[CG::kRowChunks], q1[CG::kRowChunks];
   __shared__ u32x4 g0[CG::kRowChunks], g1[CG::kRowChunks];
-  __shared__ float st0[2][64], st1[2][64];    // [LSE, D][query row]
+  __shared__ float st0[2][64], st1[2][64];    // [LSE, D (* 2^u)][query row]
+  __shared__ uint32_t red[4];
 
   const Geo g = a.g;
   const int L = blockIdx.x;                 // natural order (see common.hpp)
@@ -231,38 +292,46 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
   const size_t head_off = (size_t)bh * g.N * D;
-  const T* __restrict__ Qh = reinterpret_cast<const T*>(a.Q) + head_off;
-  const G* __restrict__ Gh = (__is_same(G, T) ? reinterpret_cast<const G*>(a.dO)
-                                               : reinterpret_cast<const G*>(a.dO16)) + head_off;
+  const G* __restrict__ Qh = (kHalf ? reinterpret_cast<const G*>(a.q16) : reinterpret_cast<const G*>(a.Q)) + head_off;
+  const G* __restrict__ Gh = (kHalf ? reinterpret_cast<const G*>(a.dO16) : reinterpret_cast<const G*>(a.dO)) + head_off;
   const float* __restrict__ LSEh = a.LSE + (size_t)bh * g.N;
-  const float* __restrict__ Dh = a.Dvec + (size_t)bh * g.N;
+  const float* __restrict__ Dh = (kHalf ? a.Du : a.Dvec) + (size_t)bh * g.N;
   const int jbase = tile_base(g, j);
 
   // this lane's key row: B fragments of S = Q K^T and dP = dO V^T (N = keys)
   const int kr = 16 * w + l16;
   const bool k_ok = kr < g.T;
   const int k_tok = jbase + (k_ok ? member_offset(g, kr) : 0);
-  Frag kf[KS];
-  GFrag vf[KS];
-  float dinv = 1.f, dpinv = 1.f;              // 2^-s of the fp16 dO copy; 2^-(s+t) for dP
-  load_row_frags16<T, D>(kf, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, q);
+  GFrag kf[KS], vf[KS];
+  // dinv: 2^-s of the fp16 dO copy (dV); dpinv: 2^(u-s-t) turns the fp16 dP into
+  // dP * 2^u; c2: the softmax scale (log2 units) over 2^(a+b); kscale: dK's 2^-u
+  float dinv = 1.f, dpinv = 1.f, c2 = a.c, kunscale = 1.f, kfac = a.scale;
   {
-    Frag vt[KS];
+    Frag kt[KS], vt[KS];
+    load_row_frags16<T, D>(kt, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, q);
     load_row_frags16<T, D>(vt, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, q);
-    float vup = 1.f;
-    if constexpr (sizeof(T) == 2) {
-      const float2 vs = a.vscale[bh];
+    float kup = 1.f, vup = 1.f;
+    if constexpr (kHalf) {
+      const int bj = block_pow2(frag_absmax(kt, KS), red, w);   // K's exponent for this key block
+      const float2 vs = a.vscale[bh], ds = a.dscale[bh];
+      const int u = ds_exponent(ds, vs, a.dabs[bh], kLog2D<D>);
+      kup = pow2f(bj);
       vup = vs.x;
-      dinv = a.dscale[bh].y;
-      dpinv = dinv * vs.y;                    // both in [2^-63, 2^63]: exact, normal
+      dinv = ds.y;
+      dpinv = dinv * vs.y * pow2f(u);         // powers of two: exact while normal
+      c2 = a.c * a.qscale[bh].y * pow2f(-bj);
+      kunscale = pow2f(-u);
+      kfac = a.scale * a.qscale[bh].y;
     }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) vf[s] = to_grad_frag(vt[s], vup, (G*)nullptr);
+    for (int s = 0; s < KS; ++s) {
+      kf[s] = to_grad_frag(kt[s], kup, (G*)nullptr);
+      vf[s] = to_grad_frag(vt[s], vup, (G*)nullptr);
+    }
   }
 
-  int qoff[DmaCfg<T, D, W>::kPer], goff[DmaCfg<G, D, W>::kPer];
-  dma_offsets<T, D, W>(qoff, g, w, lane);
-  dma_offsets<G, D, W>(goff, g, w, lane);
+  int goff[DmaCfg<G, D, W>::kPer];
+  dma_offsets<G, D, W>(goff, g, w, lane);     // the Q and dO tiles share one layout
   const int soff = lane < g.T ? member_offset(g, lane) : 0;   // stats row of lane (waves 0, 1)
 
   f32x4 dk[DT], dv[DT];
@@ -271,7 +340,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dk[t] = f32x4{};
     dv[t] = f32x4{};
   }
-  const float c2 = a.c;
   const int* list = a.entries + (size_t)bh * g.NB * a.kmax;
   const int* off = a.offsets + (size_t)bh * (g.NB + 1);
   const int e0 = off[j], n = off[j + 1] - e0;
@@ -280,12 +348,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool kFast = sizeof(T) == 2;
   const int rowl = row_lane16<D>(l16, q), trl = tr_lane16<D>(l16, q);
 
-  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Qh, (size_t)g.N * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Qh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rg = head_rsrc(Gh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rs = head_rsrc(w == 0 ? LSEh : Dh, (size_t)g.N * sizeof(float));
   auto request = [&](int tau, u32x4* lq, u32x4* lg, float (*lst)[64]) {
     const int base = tile_base(g, tau);
-    dma_tile<T, D, W>(lq, rq, base * D * (int)sizeof(T), qoff, w);
+    dma_tile<G, D, W>(lq, rq, base * D * (int)sizeof(G), goff, w);
     dma_tile<G, D, W>(lg, rg, base * D * (int)sizeof(G), goff, w);
     if (w < 2) dma_row_stats(lst[w], rs, base * 4, soff);
   };
@@ -295,21 +363,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int NS = 4 * KS;                // (mt, s) steps
     constexpr int NT = 2 * DT;                // (t, ks) steps
     // 16-bit path: operand reads run two steps ahead of the products
-    GFrag bg[4];
-    Frag bq[4];
+    GFrag bg[4], bq[4];
     if constexpr (kFast) {
-      Frag qa[3];
-      GFrag ga[3];
-      auto rd = [&](int k, Frag& qf, GFrag& gf) {
+      GFrag qa[3], ga[3];
+      auto rd = [&](int k, GFrag& qf, GFrag& gf) {
         const int xs = rowl ^ (64 * (k % KS));
-        qf = frag16_row_fast<T, D>(lq, k / KS, xs);
+        qf = frag16_row_fast<G, D>(lq, k / KS, xs);
         gf = frag16_row_fast<G, D>(lg, k / KS, xs);
       };
-      auto rt = [&](int k, GFrag& gb, Frag& qb) {   // step k = (t, ks) as in the dV/dK loop below
+      auto rt = [&](int k, GFrag& gb, GFrag& qb) {   // step k = (t, ks) as in the dV/dK loop below
         const int t = 2 * (k / 4) + (k & 1), ks = (k >> 1) & 1;
         const int xt = trl ^ (32 * t);
         gb = frag16_tr_fast<G, D>(lg, ks, xt, (G*)nullptr);
-        qb = frag16_tr_fast<T, D>(lq, ks, xt, (T*)nullptr);
+        qb = frag16_tr_fast<G, D>(lq, ks, xt, (G*)nullptr);
       };
       rd(0, qa[0], ga[0]);
       rd(1, qa[1], ga[1]);
@@ -334,15 +400,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
         pacc[mt] = f32x4{};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          sacc[mt] = mma16(frag16_row<T, D>(lq, 16 * mt + l16, s, q), kf[s], sacc[mt]);
+          sacc[mt] = mma16(frag16_row<G, D>(lq, 16 * mt + l16, s, q), kf[s], sacc[mt]);
           pacc[mt] = mma16(frag16_row<G, D>(lg, 16 * mt + l16, s, q), vf[s], pacc[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);      // bounds the operand reads in flight
       }
     }
-    // P and dS as A operands: k-slot e of step ks <-> query 32ks + 16(e/4) + 4q + e%4
-    GFrag pf[2];
-    Split sf[2];
+    // P and dS (* 2^u) as A operands: k-slot e of step ks <-> query 32ks + 16(e/4) + 4q + e%4
+    GFrag pf[2], sf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float pv[8], sv[8];
@@ -360,18 +425,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
       pf[ks] = to_frag(pv, (G*)nullptr);
-      to_split(sv, sf[ks]);
+      sf[ks] = to_frag(sv, (G*)nullptr);
     }
     __builtin_amdgcn_sched_barrier(0);
     // dV += P^T dO, dK += dS^T Q: lane holds d column 16t + l16, key rows 4q + i
     if constexpr (kFast) {
-      // steps k = (t, ks) in the order (t0, ks), (t0+1, ks) so that the hi and lo
-      // passes of dK never depend on the product issued just before them
-      auto rt = [&](int k, GFrag& gb, Frag& qb) {
+      // steps k = (t, ks) in the order (t0, ks), (t0+1, ks): no product depends on
+      // the one issued just before it
+      auto rt = [&](int k, GFrag& gb, GFrag& qb) {
         const int t = 2 * (k / 4) + (k & 1), ks = (k >> 1) & 1;
         const int xt = trl ^ (32 * t);
         gb = frag16_tr_fast<G, D>(lg, ks, xt, (G*)nullptr);
-        qb = frag16_tr_fast<T, D>(lq, ks, xt, (T*)nullptr);
+        qb = frag16_tr_fast<G, D>(lq, ks, xt, (G*)nullptr);
       };
 #pragma unroll
       for (int k = 0; k < NT; k += 2) {
@@ -381,12 +446,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int a0 = k % 4, a1 = (k + 1) % 4;
         dv[t0] = mma16(pf[ks], bg[a0], dv[t0]);
         dv[t0 + 1] = mma16(pf[ks], bg[a1], dv[t0 + 1]);
-        if constexpr (__is_same(T, bf16)) {
-          dk[t0] = mma16(sf[ks].hi, bq[a0], dk[t0]);
-          dk[t0 + 1] = mma16(sf[ks].hi, bq[a1], dk[t0 + 1]);
-          dk[t0] = mma16(sf[ks].lo, bq[a0], dk[t0]);
-          dk[t0 + 1] = mma16(sf[ks].lo, bq[a1], dk[t0 + 1]);
-        }
+        dk[t0] = mma16(sf[ks], bq[a0], dk[t0]);
+        dk[t0 + 1] = mma16(sf[ks], bq[a1], dk[t0 + 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -396,7 +457,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         for (int ks = 0; ks < 2; ++ks) {
           const int r0 = 32 * ks + 4 * q;
           dv[t] = mma16(pf[ks], frag16_tr<G, D>(lg, 16 * t, r0, l16, (G*)nullptr), dv[t]);
-          dk[t] = mma16_split_a(sf[ks], frag16_tr<T, D>(lq, 16 * t, r0, l16, (T*)nullptr), dk[t]);
+          dk[t] = mma16(sf[ks], frag16_tr<G, D>(lq, 16 * t, r0, l16, (G*)nullptr), dk[t]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -431,7 +492,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       const size_t orow = head_off + (size_t)(jbase + member_offset(g, r)) * D;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        store1(a.dK, orow + 16 * t + l16, a.out_f32, a.scale * dk[t][i]);
+        store1(a.dK, orow + 16 * t + l16, a.out_f32, (dk[t][i] * kunscale) * kfac);
         store1(a.dV, orow + 16 * t + l16, a.out_f32, dv[t][i] * dinv);
       }
     }
@@ -441,25 +502,30 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- 5. dQ
 // One work-group of 4 waves per query tile, two waves per SIMD; wave w owns
 // queries 16w..16w+15, whose Q and dO rows stay in registers as the B operands of
-// the 16x16x32 products S^T = K Q^T and dP^T = V dO^T (all bf16).  The kept
-// blocks stream through two LDS buffers (K and V rows), filled by direct
-// global->LDS loads one block ahead.  Per block and wave:
+// the 16x16x32 products S^T = K Q^T and dP^T = V dO^T.  The kept blocks stream
+// through two LDS buffers (K and V rows), filled by direct global->LDS loads one
+// block ahead.  With bf16 inputs K comes from this phase's fp16 copy (K * 2^b),
+// Q is converted to fp16 with a power of two per query tile, dP^T = V dO^T stays
+// bf16, and dS^T * 2^u is rounded to fp16.  Per block and wave:
 //   S^T, dP^T (64 keys x 16 queries)   A = K / V rows (ds_read_b128), 4 x 4 MFMA each
 //   P^T = exp2(S^T c - LSE log2 e), dS^T = P^T (dP^T - D)   lane = query column
-//   dQ^T += K^T dS^T                   B = dS^T straight from the S^T registers (bf16
-//                                      hi+lo), A = K read transposed (ds_read_b64_tr_b16)
+//   dQ^T += K^T dS^T                   B = dS^T straight from the S^T registers,
+//                                      A = K read transposed (ds_read_b64_tr_b16)
 template <typename T, int D, bool FULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<T>, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int W = 4;
+  typedef typename GradType<T>::type G;      // K tiles, Q and dS operands
   using C = TileCfg<T, D>;
+  using CG = TileCfg<G, D>;
   typedef typename Elem<T>::frag Frag;
-  typedef typename SplitOf<T>::type Split;
+  typedef typename Elem<G>::frag GFrag;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr bool kFast = sizeof(T) == 2;
-  __shared__ u32x4 k0[C::kRowChunks], k1[C::kRowChunks];
+  __shared__ u32x4 k0[CG::kRowChunks], k1[CG::kRowChunks];
   __shared__ u32x4 v0[C::kRowChunks], v1[C::kRowChunks];
+  __shared__ uint32_t red[4];
 
   const Geo g = a.g;
   const int L = blockIdx.x;                 // natural order (see common.hpp)
@@ -469,7 +535,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
   const size_t head_off = (size_t)bh * g.N * D;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(a.K) + head_off;
+  const G* __restrict__ Kh = (kFast ? reinterpret_cast<const G*>(a.k16) : reinterpret_cast<const G*>(a.K)) + head_off;
   const T* __restrict__ Vh = reinterpret_cast<const T*>(a.V) + head_off;
   const int* __restrict__ irow = a.idx + ((size_t)bh * g.NB + tau) * a.kmax;
   int kk = a.kvec[bh];
@@ -479,37 +545,57 @@ void bwd_dq_kernel(BwdArgs a) {
   const int qr = 16 * w + l16;
   const bool q_ok = qr < g.T;
   const int q_tok = tile_base(g, tau) + (q_ok ? member_offset(g, qr) : 0);
-  Frag qf[KS], gf[KS];
-  load_row_frags16<T, D>(qf, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, q);
+  GFrag qf[KS];
+  Frag gf[KS];
   load_row_frags16<T, D>(gf, reinterpret_cast<const T*>(a.dO) + head_off + (size_t)q_tok * D, q_ok, q);
   const float nl = q_ok ? -a.LSE[(size_t)bh * g.N + q_tok] * kLog2e : -INFINITY;   // padding rows: P = 0
-  const float dd = q_ok ? a.Dvec[(size_t)bh * g.N + q_tok] : 0.f;
+  float dd = q_ok ? a.Dvec[(size_t)bh * g.N + q_tok] : 0.f;
+  // c2: the softmax scale (log2 units) over 2^(a+b); up: 2^u of the fp16 dS;
+  // dQ = (acc * qunscale) * qfac
+  float c2 = a.c, up = 1.f, qunscale = 1.f, qfac = a.scale;
+  {
+    Frag qt[KS];
+    load_row_frags16<T, D>(qt, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, q);
+    float qup = 1.f;
+    if constexpr (kFast) {
+      const int at = block_pow2(frag_absmax(qt, KS), red, w);   // Q's exponent for this query tile
+      const int u = ds_exponent(a.dscale[bh], a.vscale_q[bh], a.dabs[bh], kLog2D<D>);
+      qup = pow2f(at);
+      c2 = a.c * a.kscale[bh].y * pow2f(-at);
+      up = pow2f(u);
+      dd *= up;
+      qunscale = pow2f(-u);
+      qfac = a.scale * a.kscale[bh].y;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = to_grad_frag(qt[s], qup, (G*)nullptr);
+  }
 
   int koff[DmaCfg<T, D, W>::kPer];
   dma_offsets<T, D, W>(koff, g, w, lane);
-  const __amdgpu_buffer_rsrc_t rk = head_rsrc(Kh, (size_t)g.N * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(Kh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(Vh, (size_t)g.N * D * sizeof(T));
   const int rowl = kFast ? row_lane16<D>(l16, q) : 0, trl = kFast ? tr_lane16<D>(l16, q) : 0;
 
   f32x4 dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x4{};
-  const float c2 = a.c;
 
   auto request = [&](int blk, u32x4* lk, u32x4* lv) {
     const int base = tile_base(g, blk);
-    dma_tile<T, D, W>(lk, rk, base * D * (int)sizeof(T), koff, w);
+    dma_tile<G, D, W>(lk, rk, base * D * (int)sizeof(G), koff, w);   // same layout: G and T have one size
     dma_tile<T, D, W>(lv, rv, base * D * (int)sizeof(T), koff, w);
   };
   auto compute = [&](const u32x4* lk, const u32x4* lv) {
     // S^T and dP^T: lane holds query column qr, key rows 16mt + 4q + i
     f32x4 sacc[4], pacc[4];
-    Frag ka[4];                                // transposed K operands of the first steps (prefetched)
+    GFrag ka[4];                               // transposed K operands of the first steps (prefetched)
     if constexpr (kFast) {
-      Frag ra[3], rb[3];
-      auto rd = [&](int k, Frag& x, Frag& y) {
+      GFrag ra[3];
+      Frag rb[3];
+      auto rd = [&](int k, GFrag& x, Frag& y) {
         const int xs = rowl ^ (64 * (k % KS));
-        x = frag16_row_fast<T, D>(lk, k / KS, xs);
+        x = frag16_row_fast<G, D>(lk, k / KS, xs);
         y = frag16_row_fast<T, D>(lv, k / KS, xs);
       };
       rd(0, ra[0], rb[0]);
@@ -528,8 +614,8 @@ void bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        ka[2 * k] = frag16_tr_fast<T, D>(lk, 0, trl ^ (32 * k), (T*)nullptr);
-        ka[2 * k + 1] = frag16_tr_fast<T, D>(lk, 1, trl ^ (32 * k), (T*)nullptr);
+        ka[2 * k] = frag16_tr_fast<G, D>(lk, 0, trl ^ (32 * k), (G*)nullptr);
+        ka[2 * k + 1] = frag16_tr_fast<G, D>(lk, 1, trl ^ (32 * k), (G*)nullptr);
       }
     } else {
 #pragma unroll
@@ -538,14 +624,14 @@ void bwd_dq_kernel(BwdArgs a) {
         pacc[mt] = f32x4{};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          sacc[mt] = mma16(frag16_row<T, D>(lk, 16 * mt + l16, s, q), qf[s], sacc[mt]);
+          sacc[mt] = mma16(frag16_row<G, D>(lk, 16 * mt + l16, s, q), qf[s], sacc[mt]);
           pacc[mt] = mma16(frag16_row<T, D>(lv, 16 * mt + l16, s, q), gf[s], pacc[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // dS^T as B operands: k-slot e of step ks <-> key 32ks + 16(e/4) + 4q + e%4
-    Split sf[2];
+    // dS^T (* 2^u) as B operands: k-slot e of step ks <-> key 32ks + 16(e/4) + 4q + e%4
+    GFrag sf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float sv[8];
@@ -556,33 +642,29 @@ void bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           float p = fast_exp2(fmaf(sacc[mt][i], c2, nl));
           if constexpr (!FULL) p = (16 * mt + 4 * q + i < g.T) ? p : 0.f;     // padding keys
-          sv[4 * hf + i] = p * (pacc[mt][i] - dd);
+          sv[4 * hf + i] = p * fmaf(pacc[mt][i], up, -dd);
         }
       }
-      to_split(sv, sf[ks]);
+      sf[ks] = to_frag(sv, (G*)nullptr);
     }
     __builtin_amdgcn_sched_barrier(0);
     // dQ^T += K^T dS^T: lane holds query column qr, d rows 16t + 4q + i
     if constexpr (kFast) {
-      Frag kb[4];
+      GFrag kb[4];
 #pragma unroll
       for (int t = 0; t < DT; t += 2) {
         const bool pre = t + 2 < DT;
         if (pre) {
-          kb[0] = frag16_tr_fast<T, D>(lk, 0, trl ^ (32 * (t + 2)), (T*)nullptr);
-          kb[1] = frag16_tr_fast<T, D>(lk, 1, trl ^ (32 * (t + 2)), (T*)nullptr);
-          kb[2] = frag16_tr_fast<T, D>(lk, 0, trl ^ (32 * (t + 3)), (T*)nullptr);
-          kb[3] = frag16_tr_fast<T, D>(lk, 1, trl ^ (32 * (t + 3)), (T*)nullptr);
+          kb[0] = frag16_tr_fast<G, D>(lk, 0, trl ^ (32 * (t + 2)), (G*)nullptr);
+          kb[1] = frag16_tr_fast<G, D>(lk, 1, trl ^ (32 * (t + 2)), (G*)nullptr);
+          kb[2] = frag16_tr_fast<G, D>(lk, 0, trl ^ (32 * (t + 3)), (G*)nullptr);
+          kb[3] = frag16_tr_fast<G, D>(lk, 1, trl ^ (32 * (t + 3)), (G*)nullptr);
         }
         // t: ka[0] (ks 0), ka[1] (ks 1); t+1: ka[2], ka[3]
-        dq[t] = mma16(ka[0], sf[0].hi, dq[t]);
-        dq[t + 1] = mma16(ka[2], sf[0].hi, dq[t + 1]);
-        dq[t] = mma16(ka[0], sf[0].lo, dq[t]);
-        dq[t + 1] = mma16(ka[2], sf[0].lo, dq[t + 1]);
-        dq[t] = mma16(ka[1], sf[1].hi, dq[t]);
-        dq[t + 1] = mma16(ka[3], sf[1].hi, dq[t + 1]);
-        dq[t] = mma16(ka[1], sf[1].lo, dq[t]);
-        dq[t + 1] = mma16(ka[3], sf[1].lo, dq[t + 1]);
+        dq[t] = mma16(ka[0], sf[0], dq[t]);
+        dq[t + 1] = mma16(ka[2], sf[0], dq[t + 1]);
+        dq[t] = mma16(ka[1], sf[1], dq[t]);
+        dq[t + 1] = mma16(ka[3], sf[1], dq[t + 1]);
         if (pre) {
 #pragma unroll
           for (int x = 0; x < 4; ++x) ka[x] = kb[x];
@@ -594,8 +676,8 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int t = 0; t < DT; ++t) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const Frag kt = frag16_tr<T, D>(lk, 16 * t, 32 * ks + 4 * q, l16, (T*)nullptr);
-          dq[t] = mma16(kt, sf[ks].hi, dq[t]);
+          const GFrag kt = frag16_tr<G, D>(lk, 16 * t, 32 * ks + 4 * q, l16, (G*)nullptr);
+          dq[t] = mma16(kt, sf[ks], dq[t]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -632,10 +714,10 @@ void bwd_dq_kernel(BwdArgs a) {
   // store: lane holds query column qr, d rows 16t + 4q + i
   if (q_ok) {
     const size_t orow = head_off + (size_t)q_tok * D;
-    const float sc = a.scale;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
-      store4(a.dQ, orow + 16 * t + 4 * q, a.out_f32, sc * dq[t][0], sc * dq[t][1], sc * dq[t][2], sc * dq[t][3]);
+      store4(a.dQ, orow + 16 * t + 4 * q, a.out_f32, (dq[t][0] * qunscale) * qfac, (dq[t][1] * qunscale) * qfac,
+             (dq[t][2] * qunscale) * qfac, (dq[t][3] * qunscale) * qfac);
   }
 }
 
@@ -651,6 +733,10 @@ hipError_t launch_prepare_t(const BwdArgs& a, hipStream_t s) {
   const size_t pgrid = (tokens + tpb - 1) / tpb;
   hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)(pgrid < (1u << 20) ? pgrid : (1u << 20))), dim3(256), 0,
                      s, a);
+  if constexpr (sizeof(T) == 2) {
+    const hipError_t e = launch_absmax_f32(a.Dvec, a.BH, (size_t)a.g.N, a.dabs_part, a.dabs, s);
+    if (e != hipSuccess) return e;
+  }
   const size_t nwords = (size_t)a.BH * a.g.NB * a.words;
   const unsigned zgrid = (unsigned)((nwords + 255) / 256 < 65536 ? (nwords + 255) / 256 : 65536);
   hipLaunchKernelGGL(zero_words_kernel, dim3(zgrid), dim3(256), 0, s, a.bitmap, nwords);
@@ -674,7 +760,13 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, int io_f32, int d, hipStream_t s
 template <typename T, int D>
 void launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (launch_pow2_scale(a.V, a.BH, (size_t)a.g.N * D, a.vmax, a.vscale, s) != hipSuccess) return;
+    // V's and Q's scales, the fp16 copy of Q, then D * 2^u
+    const size_t per_head = (size_t)a.g.N * D;
+    if (launch_pow2_scale(a.V, a.BH, per_head, a.vmax, a.vscale, s) != hipSuccess) return;
+    if (launch_pow2_scale(a.Q, a.BH, per_head, a.qmax, a.qscale, s) != hipSuccess) return;
+    if (launch_pow2_convert(a.Q, a.BH, per_head, a.qscale, a.q16, s) != hipSuccess) return;
+    const unsigned gx = (unsigned)((a.g.N + 255) / 256 < 64 ? (a.g.N + 255) / 256 : 64);
+    hipLaunchKernelGGL((scale_d_kernel<D>), dim3(gx, (unsigned)a.BH), dim3(256), 0, s, a);
   }
   const dim3 grid(a.BH * a.g.NB), block(256);
   if (a.g.T == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, s, a);
@@ -693,6 +785,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int io_f32, int d, hipStream_t s) {
 
 template <typename T, int D>
 void launch_dq_t(const BwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // V's scale (for the exponent of dS), K's scale and the fp16 copy of K
+    const size_t per_head = (size_t)a.g.N * D;
+    if (launch_pow2_scale(a.V, a.BH, per_head, a.vmax_q, a.vscale_q, s) != hipSuccess) return;
+    if (launch_pow2_scale(a.K, a.BH, per_head, a.kmaxp, a.kscale, s) != hipSuccess) return;
+    if (launch_pow2_convert(a.K, a.BH, per_head, a.kscale, a.k16, s) != hipSuccess) return;
+  }
   const dim3 grid(a.BH * a.g.NB), block(256);
   if (a.g.T == 64) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), grid, block, 0, s, a);

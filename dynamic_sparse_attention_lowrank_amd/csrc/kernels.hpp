@@ -115,6 +115,14 @@ constexpr int kDoChunks = 64;
 // an all-zero head).  `partial` holds BH * kDoChunks words.
 hipError_t launch_pow2_scale(const void* X, int BH, size_t elems_per_head, uint32_t* partial, float2* scale,
                              hipStream_t s);
+// out = fp16(X * scale[bh].x) for a bf16 [BH][elems_per_head] tensor (the exact
+// fp16 copy that the power-of-two scale above makes possible)
+hipError_t launch_pow2_convert(const void* X, int BH, size_t elems_per_head, const float2* scale, void* out,
+                               hipStream_t s);
+// out[bh] = bit pattern of max |X| over the head's elems_per_head floats (an order-free
+// maximum of the magnitude bits; a NaN anywhere gives a pattern above +inf's)
+hipError_t launch_absmax_f32(const float* X, int BH, size_t elems_per_head, uint32_t* partial, uint32_t* out,
+                             hipStream_t s);
 
 struct BwdArgs {
   const void* Q;
@@ -139,6 +147,18 @@ struct BwdArgs {
   float2* dscale;       // [BH] (2^s_bh, 2^-s_bh): the fp16 copy's exact power-of-two scale
   uint32_t* vmax;       // [BH, kDoChunks] partial max |V| (bf16 inputs; written by the dK/dV phase)
   float2* vscale;       // [BH] (2^t_bh, 2^-t_bh): scale of V before its fp16 conversion in dK/dV
+  // bf16 inputs: the fp16 dS products (see attn_bwd.hip)
+  uint32_t* dabs;       // [BH] bits of max |D| (written by prepare)
+  uint32_t* dabs_part;  // [BH, kDoChunks] its partial maxima
+  float* Du;            // [BH, N] D * 2^u_bh, the scaled D of the dK/dV phase
+  void* q16;            // [BH, N, d] fp16 Q * 2^a_bh (dK/dV phase)
+  uint32_t* qmax;       // [BH, kDoChunks]
+  float2* qscale;       // [BH] (2^a_bh, 2^-a_bh)
+  void* k16;            // [BH, N, d] fp16 K * 2^b_bh (dQ phase)
+  uint32_t* kmaxp;      // [BH, kDoChunks]
+  float2* kscale;       // [BH] (2^b_bh, 2^-b_bh)
+  uint32_t* vmax_q;     // [BH, kDoChunks] partial max |V| of the dQ phase
+  float2* vscale_q;     // [BH] V's scale as the dQ phase computes it (same values as vscale)
   uint32_t* bitmap;     // [BH, NB, words]   bit tau of row j: tile tau kept block j
   int32_t* counts;      // [BH, NB]
   int32_t* offsets;     // [BH, NB + 1]

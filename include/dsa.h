@@ -256,9 +256,11 @@ DSA_API dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, c
  * the reverse (key block -> query tiles) index of idx (for every key block, the
  * query tiles whose kept set contains it: the sums over queries of dK and dV in
  * the DSV page's stage two, section 4, run over these lists) and, for bf16
- * inputs, an fp16 copy of dO (B*H*N*d*2 bytes) for the fp16 products of the
- * backward, with the per-(b, h) scales of dO and of V (for each, B*H*64 partial
- * maxima and B*H float pairs).  Sections are 256-byte aligned.
+ * inputs, what the fp16 products of the backward need: fp16 copies of dO, of Q
+ * (dK/dV phase) and of K (dQ phase), B*H*N*d*2 bytes each; the power-of-two
+ * scales of dO, V, Q, K and of V again for the dQ phase (for each, B*H*64 partial
+ * maxima and B*H float pairs); max |D| per (b, h) with its B*H*64 partial maxima;
+ * and D times the fp16 dS scale (B*H*N floats).  Sections are 256-byte aligned.
  */
 DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
 
@@ -278,14 +280,16 @@ DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax
  *   dQ, dK, dV: outputs [B,H,N,d] of out_dtype, fully overwritten.
  *   workspace: device memory of at least dsa_attn_bwd_workspace_bytes(shape, kmax)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
- *   Precision with bf16 inputs: dV = P^T dO and dP = dO V^T run on fp16 matrix
- *   cores (P in [0,1] rounded to fp16; dO and V converted to fp16 after
- *   multiplying each by its own power of two per (b, h) that puts the head's
- *   largest magnitude in [2^14, 2^15), so the conversions are exact for every
- *   element within a factor 2^31 of that maximum, whatever the size of the
- *   gradients and values; the products are scaled back in fp32, exactly);
- *   products with dS use a bf16 hi+lo pair (two matrix-core passes), so their
- *   accuracy does not depend on the scale of dS.
+ *   Precision with bf16 inputs: every product runs on fp16 matrix cores.  dO, V,
+ *   Q and K are converted to fp16 after multiplying each by a power of two that
+ *   puts its largest magnitude (per (b, h), or per 64-row block for the rows a
+ *   work-group keeps in registers) in [2^14, 2^15), so the conversions are exact
+ *   for every element within a factor 2^31 of that maximum, whatever the size of
+ *   the inputs; P in [0,1] is rounded to fp16; dS is rounded to fp16 after a
+ *   power of two per (b, h) derived from bounds on |dO . v| and |D| that hold for
+ *   every element (no overflow; 2^-12 relative for every value within 2^-29 of
+ *   the bound).  All powers of two are taken back out in fp32, exactly, so
+ *   scaling dO or V by a power of two scales the gradients exactly.
  *   The same device-side robustness rules as dsa_attn_fwd apply.
  */
 DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const void* K, const void* V,
@@ -298,15 +302,18 @@ DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const voi
  * Backward in phases.  dsa_attn_bwd is exactly these three calls in order on one
  * stream; callers may instead issue them separately, e.g. run dsa_attn_bwd_dkdv
  * and dsa_attn_bwd_dq concurrently on two streams once dsa_attn_bwd_prepare has
- * completed (both only read the workspace).  Arguments mean what they mean for
- * dsa_attn_bwd; the workspace must be the one prepared with the same idx, k,
- * kmax, O and dO.
+ * completed (each reads what prepare wrote and writes only workspace sections of
+ * its own).  Arguments mean what they mean for dsa_attn_bwd; the workspace must
+ * be the one prepared with the same idx, k, kmax, O and dO.
  *
  * dsa_attn_bwd_prepare -- D = rowsum(dO * O) and the reverse index (for every
- *   key block, the ascending list of query tiles that kept it) into the workspace.
+ *   key block, the ascending list of query tiles that kept it) into the
+ *   workspace (bf16: also dO's scale and fp16 copy, and max |D|).
  * dsa_attn_bwd_dkdv    -- dK, dV: one pass per key block over the query tiles
- *   that kept it (it first finds V's power-of-two scale into the workspace).
- * dsa_attn_bwd_dq      -- dQ: one pass per query tile over its kept blocks.
+ *   that kept it (bf16: it first writes V's and Q's scales, Q's fp16 copy and the
+ *   scaled D into its sections).
+ * dsa_attn_bwd_dq      -- dQ: one pass per query tile over its kept blocks
+ *   (bf16: it first writes V's and K's scales and K's fp16 copy into its sections).
  */
 DSA_API dsa_status dsa_attn_bwd_prepare(const dsa_shape* shape, const void* O, int32_t o_dtype, const void* dO,
                                         const int32_t* idx, const int32_t* k, int32_t kmax, void* workspace,
