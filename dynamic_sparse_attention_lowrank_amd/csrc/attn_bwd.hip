@@ -298,6 +298,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const float* __restrict__ Dh = (kHalf ? a.Du : a.Dvec) + (size_t)bh * g.N;
   const int jbase = tile_base(g, j);
 
+  // Reduction order of the 16x16x32 products that read row operands from LDS (S, dP):
+  // lane group q takes the 8-element chunk qk of each 32-wide step, the two bits of
+  // q swapped (16-bit tiles).  Measured on gfx950: when lanes l and l+32 read one row
+  // at chunks that differ in bit 1, every ds_read_b128 pays a second pass (LDS bank
+  // conflict counters: 4 of 8 cycles); chunks that differ in bit 0 cost nothing.
+  const int qk = kHalf ? (((q & 1) << 1) | (q >> 1)) : q;
   // this lane's key row: B fragments of S = Q K^T and dP = dO V^T (N = keys)
   const int kr = 16 * w + l16;
   const bool k_ok = kr < g.T;
@@ -308,8 +314,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   float dinv = 1.f, dpinv = 1.f, c2 = a.c, kunscale = 1.f, kfac = a.scale;
   {
     Frag kt[KS], vt[KS];
-    load_row_frags16<T, D>(kt, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, q);
-    load_row_frags16<T, D>(vt, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, q);
+    load_row_frags16<T, D>(kt, reinterpret_cast<const T*>(a.K) + head_off + (size_t)k_tok * D, k_ok, qk);
+    load_row_frags16<T, D>(vt, reinterpret_cast<const T*>(a.V) + head_off + (size_t)k_tok * D, k_ok, qk);
     float kup = 1.f, vup = 1.f;
     if constexpr (kHalf) {
       const int bj = block_pow2(frag_absmax(kt, KS), red, w);   // K's exponent for this key block
@@ -346,7 +352,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   // 16-bit tiles: closed-form operand addresses (one lane constant each)
   constexpr bool kFast = sizeof(T) == 2;
-  const int rowl = row_lane16<D>(l16, q), trl = tr_lane16<D>(l16, q);
+  const int rowl = row_lane16<D>(l16, qk), trl = tr_lane16<D>(l16, q);
 
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(Qh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rg = head_rsrc(Gh, (size_t)g.N * D * sizeof(G));
@@ -541,13 +547,16 @@ void bwd_dq_kernel(BwdArgs a) {
   int kk = a.kvec[bh];
   kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
 
+  // reduction order of S^T and dP^T: lane group q takes chunk qk of each 32-wide step
+  // (the bits of q swapped for 16-bit tiles; see the dK/dV kernel)
+  const int qk = kFast ? (((q & 1) << 1) | (q >> 1)) : q;
   // this lane's query row (B fragments: N = queries)
   const int qr = 16 * w + l16;
   const bool q_ok = qr < g.T;
   const int q_tok = tile_base(g, tau) + (q_ok ? member_offset(g, qr) : 0);
   GFrag qf[KS];
   Frag gf[KS];
-  load_row_frags16<T, D>(gf, reinterpret_cast<const T*>(a.dO) + head_off + (size_t)q_tok * D, q_ok, q);
+  load_row_frags16<T, D>(gf, reinterpret_cast<const T*>(a.dO) + head_off + (size_t)q_tok * D, q_ok, qk);
   const float nl = q_ok ? -a.LSE[(size_t)bh * g.N + q_tok] * kLog2e : -INFINITY;   // padding rows: P = 0
   float dd = q_ok ? a.Dvec[(size_t)bh * g.N + q_tok] : 0.f;
   // c2: the softmax scale (log2 units) over 2^(a+b); up: 2^u of the fp16 dS;
@@ -555,7 +564,7 @@ void bwd_dq_kernel(BwdArgs a) {
   float c2 = a.c, up = 1.f, qunscale = 1.f, qfac = a.scale;
   {
     Frag qt[KS];
-    load_row_frags16<T, D>(qt, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, q);
+    load_row_frags16<T, D>(qt, reinterpret_cast<const T*>(a.Q) + head_off + (size_t)q_tok * D, q_ok, qk);
     float qup = 1.f;
     if constexpr (kFast) {
       const int at = block_pow2(frag_absmax(qt, KS), red, w);   // Q's exponent for this query tile
@@ -575,7 +584,7 @@ void bwd_dq_kernel(BwdArgs a) {
   dma_offsets<T, D, W>(koff, g, w, lane);
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(Kh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(Vh, (size_t)g.N * D * sizeof(T));
-  const int rowl = kFast ? row_lane16<D>(l16, q) : 0, trl = kFast ? tr_lane16<D>(l16, q) : 0;
+  const int rowl = kFast ? row_lane16<D>(l16, qk) : 0, trl = kFast ? tr_lane16<D>(l16, q) : 0;
 
   f32x4 dq[DT];
 #pragma unroll
