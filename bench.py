@@ -10,12 +10,19 @@ kept (k = 52), bf16 inputs.  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is attended TFLOP/s of the whole step with the
 attended work counted as 4*d FLOP per (query, key) pair forward and 10*d
-backward; `roofline` describes the dominant kernel, timed with HIP events on
-the stream it runs on; `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload (rank 0, one GPU only).  `phase_stats_ms` gives the
-median / min / max of every phase over the timed steps, `fwd_cold` the forward
-alone after a 512 MiB cache-evicting write (L2 and memory-attached cache cold),
-`clocks` the engine / memory clock levels read from sysfs before and after.
+backward (workloads without a backward: forward only).  `headline` is the
+layer's forward alone, the median of 20 repetitions each after a 512 MiB
+cache-evicting write (L2 and memory-attached cache cold); `fwd` gives the same
+call warm, inside the steps.  `roofline` describes the dominant kernel (its
+algorithmic FLOP: forward 4*d, dK/dV 8*d, dQ 2*d per pair -- the dQ pass's
+recomputation of S and dP is not counted), timed with HIP events on the stream
+it runs on, beside the average duration of the same kernel in the committed
+rocprofv3 trace when that trace was taken on the current sources;
+`bwd_roofline` is the whole backward at 10*d.  `cpu_baseline` times the fp64
+oracle per phase on a bounded sample of this workload and of the other
+configurations (one GPU only).  `phase_stats_ms` gives the median / min / max
+of every phase over the timed steps, `clocks` the engine / memory clock levels
+read from sysfs before and after.
 """
 from __future__ import annotations
 
@@ -45,10 +52,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train_32k")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--cpu-configs", default="tiny_fp32,layer_32k,long_524k,dynamic_55k",
+                    help="other configurations the oracle baseline also samples (comma list; empty: none)")
+    ap.add_argument("--cpu-config-seconds", type=float, default=3.0,
+                    help="oracle budget per configuration of --cpu-configs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-reps", type=int, default=10,
-                    help="repetitions of the forward alone after a 512 MiB cache-evicting write")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="repetitions of the forward alone after a 512 MiB cache-evicting write (the headline)")
     ap.add_argument("--score-matrix", action="store_true",
                     help="predict (writes the NB x NB scores) then select, instead of the fused entry point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -126,51 +137,132 @@ def load_traffic(kernel: str, workload: str, prof_dir: Optional[str] = None):
         return None
 
 
-def cpu_baseline(x, wl, seconds: float):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload: heads in
-    order, each head's pooled predictor, then its query tiles in a fixed shuffled
-    order (score row, top-k selection, forward and backward of the tile) until the
-    time budget is spent (whole tiles only)."""
-    import numpy as np
-    import oracle
+def load_trace_avg_us(kernel: str, workload: str, prof_dir: Optional[str] = None):
+    """Average duration (us) of the kernel's bf16 d = 128 variant in the committed
+    rocprofv3 kernel-trace summary, if that summary was taken on the current kernel
+    sources (else None)."""
+    path = os.path.join(prof_dir or os.path.join(ROOT, "profiles"), f"{workload}_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"source_hash {source_hash()}" not in text:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and cells[0].startswith(kernel + "<bf16,128"):
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Threads the oracle's BLAS uses (its only multi-threaded part)."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+        return max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_sample(x, wl, seconds: float, with_bwd: bool):
+    """The fp64 oracle, as it stands, on a bounded sample of one workload: heads in
+    order, each head's pooled predictor, then its query tiles in a fixed shuffled
+    order (score row, top-k selection, forward and, for training workloads,
+    backward of the tile) until the time budget is spent (whole tiles only).  Wall
+    time per phase, and each phase extrapolated to the whole workload (pooling by
+    heads, score rows and selection by tiles, forward and backward by attended
+    pairs)."""
+    import oracle
     f = lambda t: t.detach().cpu().double().numpy()
     geom = oracle.Geometry(*wl.latent, *wl.tile)
     mem = geom.members()
     scale = 1.0 / math.sqrt(wl.d)
     T = geom.T
     order = np.random.default_rng(0).permutation(geom.NB)
-    flops, tiles, heads, busy = 0.0, 0, 0, 0.0
+    ph = {"predict": 0.0, "select": 0.0, "fwd": 0.0, "bwd": 0.0}
+    pool_s, tiles, heads, pairs = 0.0, 0, 0, 0
+    names = ("Q", "K", "V", "dO") if with_bwd else ("Q", "K", "V")
+    ks = [int(v) for v in x["k"].tolist()]
     for bh in range(wl.B * wl.H):
         b, h = divmod(bh, wl.H)
-        Q, K, V, dO = (f(x[n][b, h]) for n in ("Q", "K", "V", "dO"))      # staging, not timed
+        arr = {n: f(x[n][b, h]) for n in names}                 # staging, not timed
         Wq, Wk = f(x["Wq"][h]), f(x["Wk"][h])
-        k = int(x["k"][bh])
-        t0 = time.perf_counter()
-        Qb = oracle.pooled_features(Q, Wq, mem)
-        Kb = oracle.pooled_features(K, Wk, mem)
+        k = ks[bh]
+        c0 = time.perf_counter()
+        Qb = oracle.pooled_features(arr["Q"], Wq, mem)
+        Kb = oracle.pooled_features(arr["K"], Wk, mem)
+        dt = time.perf_counter() - c0
+        ph["predict"] += dt
+        pool_s += dt
         heads += 1
         for tau in order:
+            t0 = time.perf_counter()
             srow = oracle.block_scores(Qb[tau:tau + 1], Kb)[0]
+            t1 = time.perf_counter()
             blocks = list(oracle.select_row(srow, int(tau), k))
-            oracle.attn_tile(Q, K, V, mem, int(tau), blocks, scale)
-            oracle.attn_bwd_tile(Q, K, V, dO, mem, int(tau), blocks, scale)
-            flops += 14.0 * wl.d * T * (k * T)
+            t2 = time.perf_counter()
+            oracle.attn_tile(arr["Q"], arr["K"], arr["V"], mem, int(tau), blocks, scale)
+            t3 = time.perf_counter()
+            if with_bwd:
+                oracle.attn_bwd_tile(arr["Q"], arr["K"], arr["V"], arr["dO"], mem, int(tau), blocks, scale)
+            t4 = time.perf_counter()
+            ph["predict"] += t1 - t0
+            ph["select"] += t2 - t1
+            ph["fwd"] += t3 - t2
+            ph["bwd"] += t4 - t3
             tiles += 1
-            if busy + time.perf_counter() - t0 >= seconds:
+            pairs += k * T * T
+            if sum(ph.values()) >= seconds:
                 break
-        busy += time.perf_counter() - t0
-        if busy >= seconds:
+        if sum(ph.values()) >= seconds:
             break
-    return {"value": flops / busy / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{wl.name}: {tiles} query tiles over {heads} head(s) of {wl.B * wl.H} "
-                      f"({geom.NB} tiles per head): per head the pooled predictor, per tile its score row, "
-                      f"top-k selection and fp64 forward + backward; {busy:.1f} s of oracle time; "
-                      f"value = counted attended FLOP (14*d per pair) of the sample / that time"}
+    total_tiles = wl.B * wl.H * geom.NB
+    total_pairs = sum(geom.NB * kk * T * T for kk in ks)
+    full = {"predict": pool_s * (wl.B * wl.H) / heads + (ph["predict"] - pool_s) * total_tiles / tiles,
+            "select": ph["select"] * total_tiles / tiles,
+            "fwd": ph["fwd"] * total_pairs / pairs,
+            "bwd": ph["bwd"] * total_pairs / pairs if with_bwd else 0.0}
+    fl_per_pair = (14.0 if with_bwd else 4.0) * wl.d
+    busy = sum(ph.values())
+    return {"value": fl_per_pair * pairs / busy / 1e12, "unit": "TFLOP/s",
+            "phases_s": {p: round(v, 4) for p, v in ph.items() if with_bwd or p != "bwd"},
+            "extrapolated_full_s": {p: round(v, 2) for p, v in full.items() if with_bwd or p != "bwd"},
+            "sample": f"{wl.name}: {tiles} of {total_tiles} query tiles over {heads} head(s) of {wl.B * wl.H}: "
+                      f"per head the pooled predictor, per tile its score row, top-k selection and fp64 forward"
+                      f"{' + backward' if with_bwd else ''}; {busy:.1f} s of oracle time; value = counted "
+                      f"attended FLOP ({int(fl_per_pair / wl.d)}*d per pair) of the sample / that time; the "
+                      f"full-workload times are extrapolated from the sample"}
+
+
+def cpu_baseline(x, wl, seconds: float, others, per_config: float, dev):
+    """cpu_sample on this workload (x) and on each configuration in `others`
+    (inputs generated on the device like the bench's, then staged to the host)."""
+    from dsa_inputs import WORKLOADS, generate
+    out = cpu_sample(x, wl, seconds, with_bwd=wl.backward)
+    out.update({"cores": oracle_threads(), "cpu_model": cpu_model(), "kind": "oracle"})
+    cfgs = {}
+    for name in others:
+        if name == wl.name or name not in WORKLOADS:
+            continue
+        w2 = WORKLOADS[name]
+        x2 = generate(w2, device=dev, with_grad=w2.backward)
+        cfgs[name] = cpu_sample(x2, w2, per_config, with_bwd=w2.backward)
+        del x2
+    out["configs"] = cfgs
+    return out
 
 
 def main():
@@ -197,7 +289,7 @@ def main():
         sys.exit(1)
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    x = generate(wl, device=dev, with_grad=True)
+    x = generate(wl, device=dev, with_grad=wl.backward)
     lay = dsa.Layout(tuple(wl.latent), tuple(wl.tile))
     B, H, N, d, NB, T = wl.B, wl.H, wl.N, wl.d, wl.NB, wl.T
     kdev = x["k"].to(dev)
@@ -214,13 +306,18 @@ def main():
     dQ = torch.empty(B, H, N, d, device=dev, dtype=torch.bfloat16)
     dK = torch.empty_like(dQ)
     dV = torch.empty_like(dQ)
-    ws = torch.empty(dsa.bwd_workspace_bytes(x["Q"], lay, kmax), device=dev, dtype=torch.uint8)
+    ws = (torch.empty(dsa.bwd_workspace_bytes(x["Q"], lay, kmax), device=dev, dtype=torch.uint8)
+          if wl.backward else None)
     fws = torch.empty(dsa.fwd_workspace_bytes(x["Q"], lay), device=dev, dtype=torch.uint8)
-    Q, K, V, dO, Wq, Wk = (x[n] for n in ("Q", "K", "V", "dO", "Wq", "Wk"))
+    Q, K, V, Wq, Wk = (x[n] for n in ("Q", "K", "V", "Wq", "Wk"))
+    dO = x.get("dO")
 
+    train = wl.backward                       # forward-only workloads skip the backward phases
     phases = ["predict", "select", "fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq"]
     if not args.score_matrix:
         phases[0:2] = ["predict_select", "-"]
+    if not train:
+        phases = phases[:3]
 
     def step(ev=None):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
@@ -236,6 +333,8 @@ def main():
         rec(2)
         dsa.attn_fwd(Q, K, V, idx, kdev, lay, out=(O, LSE), workspace=fws)
         rec(3)
+        if not train:
+            return
         dsa.attn_bwd_prepare(O, dO, idx, kdev, lay, ws)
         rec(4)
         dsa.attn_bwd_dkdv(Q, K, V, dO, LSE, kmax, lay, ws, dK, dV)
@@ -324,15 +423,17 @@ def main():
 
     pairs = sum(NB * kk * T * T for kk in ks)          # attended (query, key) pairs
     flop_fwd = 4.0 * d * pairs
-    flop_bwd = 10.0 * d * pairs
+    flop_bwd = 10.0 * d * pairs if train else 0.0
     flop_step = flop_fwd + flop_bwd
     value = flop_step / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = flop_fwd / (phase_ms["fwd"] * 1e-3) / 1e12
 
-    # dominant single-kernel phase and its algorithmic work per launch
-    algo = {"fwd": (4.0 * d * pairs, "attn_fwd_kernel"),
-            "bwd_dkdv": (8.0 * d * pairs, "bwd_dkdv_kernel"),
-            "bwd_dq": (6.0 * d * pairs, "bwd_dq_kernel")}
+    # dominant single-kernel phase and its algorithmic work per launch: forward 4*d
+    # per pair; dK/dV 8*d (S, dP, dV, dK); dQ 2*d (dQ only: its recomputation of S
+    # and dP is extra work, not algorithmic)
+    algo = {"fwd": (4.0 * d * pairs, "attn_fwd_kernel")}
+    if train:
+        algo.update({"bwd_dkdv": (8.0 * d * pairs, "bwd_dkdv_kernel"), "bwd_dq": (2.0 * d * pairs, "bwd_dq_kernel")})
     dom = max(algo, key=lambda p: phase_ms[p])
     achieved = algo[dom][0] / (phase_ms[dom] * 1e-3) / 1e12
     traffic = load_traffic(algo[dom][1], wl.name)
@@ -340,6 +441,21 @@ def main():
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": algo[dom][1], "ms": round(phase_ms[dom], 4),
                 "algorithmic_flop_per_launch": algo[dom][0]}
+    # the same kernel's average duration in the committed rocprofv3 trace (when it
+    # was taken on the current sources) and the fraction it gives
+    tr = load_trace_avg_us(algo[dom][1], wl.name)
+    if tr is not None:
+        roofline["rocprof_avg_ms"] = round(tr / 1e3, 4)
+        roofline["frac_at_rocprof_avg"] = round(algo[dom][0] / (tr * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    bwd_roofline = None
+    if train:
+        bwd_ms = phase_ms["bwd_prepare"] + phase_ms["bwd_dkdv"] + phase_ms["bwd_dq"]
+        bwd_tf = flop_bwd / (bwd_ms * 1e-3) / 1e12
+        bwd_roofline = {"bound": "mfma", "what": "prepare + dK/dV + dQ, 10*d FLOP per pair", "ms": round(bwd_ms, 4),
+                        "achieved": round(bwd_tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(bwd_tf / BF16_PEAK_TFLOPS, 4)}
+    cold_med = float(np.median(cold)) if cold else None
+    cold_tf = flop_fwd / (cold_med * 1e-3) / 1e12 if cold else None
 
     out = {
         "metric": METRIC,
@@ -354,12 +470,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: one attention layer, training step (predict+select+fwd+bwd)",
+        "config": {"workload": f"{wl.name}: one attention layer, " + ("training step (predict+select+fwd+bwd)"
+                                                                       if train else "forward (predict+select+fwd)"),
                    "predictor": "two-step (score matrix)" if args.score_matrix else "fused predict+select",
                    "B": B, "H": H, "d": d, "latent": list(wl.latent), "tokens": N, "tile": list(wl.tile),
                    "blocks": NB, "rank": r, "k": kmax, "keep_percent": list(wl.keep_percent)},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
-        "fwd": {"ms": round(phase_ms["fwd"], 4), "tflops": round(fwd_tflops, 2),
+        "headline": {"what": f"dsa_attn_fwd alone, median of {len(cold)} repetitions each after a 512 MiB "
+                             "cache-evicting write (L2 and memory-attached cache cold)",
+                     "ms_per_layer": round(cold_med, 4), "tflops": round(cold_tf, 2),
+                     "pct_bf16_peak": round(100 * cold_tf / BF16_PEAK_TFLOPS, 2),
+                     "pct_bf16_peak_at_measured_sclk": pct_at_clock(cold_tf, clocks_start, clocks_end)}
+                    if cold else None,
+        "fwd": {"what": "warm, inside the timed steps", "ms": round(phase_ms["fwd"], 4), "tflops": round(fwd_tflops, 2),
                 "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2),
                 "pct_bf16_peak_at_measured_sclk": pct_at_clock(fwd_tflops, clocks_start, clocks_end)},
         "phase_ms": {p: round(v, 4) for p, v in phase_ms.items() if p != "-"},
@@ -371,6 +494,7 @@ def main():
         "event_ms_per_step": round(span_ms, 4),
         "counted_flop": {"fwd": flop_fwd, "bwd": flop_bwd, "pairs": pairs},
         "roofline": roofline,
+        "bwd_roofline": bwd_roofline,
         "rope3d": {"ms": round(rope_ms, 4), "what": "Q, K rotated + dQ, dK rotated back", "bound": "hbm",
                    "algorithmic_bytes": rope_bytes, "GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
                    "peak_GBps": 8000.0},
@@ -379,7 +503,8 @@ def main():
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
+        others = [c for c in args.cpu_configs.split(",") if c]
+        out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds, others, args.cpu_config_seconds, dev)
     print(json.dumps(out), flush=True)
 
 
@@ -456,6 +581,12 @@ def summarize(root: str, prof_dir: Optional[str] = None):
     stats = glob.glob(os.path.join(root, "trace", "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = [r for r in csv.DictReader(open(stats)) if _is_library_kernel(r["Name"])]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    # launch resources as the profiler reports them (first dispatch of each kernel)
+    res = {}
+    for f in glob.glob(os.path.join(root, "trace", "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if _is_library_kernel(r["Kernel_Name"]):
+                res.setdefault(_kernel_label(r["Kernel_Name"]), r)
     c = out["config"]
     lines = [f"# Kernel trace: {wl_name} training step (B={c['B']} H={c['H']} d={c['d']}, {c['tokens']:,} tokens, "
              f"tile {'x'.join(map(str, c['tile']))}, k={c['k']}, bf16)", "",
@@ -463,14 +594,23 @@ def summarize(root: str, prof_dir: Optional[str] = None):
              f"Library sources: source_hash {out['source_hash']} (bench.py prints the same hash).", "",
              f"Library kernels only ({out['warmup']} warm-up + {out['steps']} timed steps per kernel); "
              "the other rows of the raw summary are torch's input generator.", "",
-             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+             "Launch resources as the kernel trace reports them: VGPR / AGPR (VGPR_Count, "
+             "Accum_VGPR_Count), LDS bytes per work-group (LDS_Block_Size), scratch bytes per lane "
+             "(Scratch_Size), work-group size.", "",
+             "| kernel | calls | avg us | min us | max us | VGPR | AGPR | LDS B | scratch B | WG |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        lab = _kernel_label(r["Name"])
+        rr = res.get(lab, {})
+        g = lambda k: rr.get(k, "-")
+        lines.append(f"| {lab} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {g('VGPR_Count')} | "
+                     f"{g('Accum_VGPR_Count')} | {g('LDS_Block_Size')} | {g('Scratch_Size')} | "
+                     f"{g('Workgroup_Size_X')} |")
     lines += ["", "In-bench HIP-event phase times of the same run, ms:", "",
               "    " + json.dumps(out["phase_ms"]), "",
               f"Step {out['ms_per_step']} ms, {out['value']} attended TFLOP/s; forward {out['fwd']['ms']} ms = "
-              f"{out['fwd']['tflops']} TFLOP/s (the profiler's serialisation inflates the step slightly)."]
+              f"{out['fwd']['tflops']} TFLOP/s warm (the profiler's serialisation inflates the step slightly)."]
     with open(os.path.join(prof, f"{wl_name}_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -523,10 +663,11 @@ def summarize(root: str, prof_dir: Optional[str] = None):
 
 
 # per attention kernel: counts of SQ / TA / TCP events per dispatch, and the same
-# per (wave, block) unit -- one wave's 32-key half of one kept block (forward), one
-# wave's 16 keys against one query tile (dK/dV) or its 16 queries against one kept
-# block (dQ) -- so that instruction mixes and unit busy times compare across kernels
-_UNITS = {"attn_fwd_kernel": 2, "bwd_dkdv_kernel": 4, "bwd_dq_kernel": 4}
+# per (wave, block) unit -- one wave's 32 queries x 32 keys of one kept block
+# (forward), one wave's 16 keys against one query tile (dK/dV) or its 16 queries
+# against one kept block (dQ): four waves share each (query tile, kept block) pair
+# in every kernel -- so that instruction mixes and unit busy times compare
+_UNITS = {"attn_fwd_kernel": 4, "bwd_dkdv_kernel": 4, "bwd_dq_kernel": 4}
 
 
 def summarize_counters(root: str, wl_name: str, src_hash: str, prof: str):
@@ -560,17 +701,31 @@ def summarize_counters(root: str, wl_name: str, src_hash: str, prof: str):
               "Per dispatch: the counter summed over all its instances, averaged over the dispatches of "
               "the run. Per unit: divided by the number of (wave, block) units of one launch -- "
               f"{blocks:.0f} (query tile, kept block) pairs times the waves that share one pair "
-              "(2 in the forward, 4 in dK/dV and dQ).", ""]
+              "(4 in each kernel).", ""]
     names = sorted({c for k in vals.values() for c in k})
+    raw = ("SQ_", "TA_", "TD_", "TCC_", "TCP_", "GRBM_")
     for label in sorted(vals):
         units = blocks * _UNITS[label.split("<")[0]]
         lines += [f"## {label}", "", "| counter | per dispatch | per unit |", "|---|---|---|"]
+        avg = {}
         for c in names:
             if c not in vals[label]:
                 continue
             v = list(vals[label][c].values())
-            avg = sum(v) / len(v)
-            lines.append(f"| {c} | {avg:.4g} | {avg / units:.1f} |")
+            avg[c] = sum(v) / len(v)
+            # derived metrics (percentages, mean occupancy) are per dispatch only
+            per_unit = f"{avg[c] / units:.1f}" if c.startswith(raw) else "-"
+            lines.append(f"| {c} | {avg[c]:.4g} | {per_unit} |")
+        extra = []
+        if avg.get("TCC_HIT_sum") is not None and avg.get("TCC_MISS_sum") is not None:
+            tot = avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"]
+            if tot > 0:
+                extra.append(f"L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS): {100 * avg['TCC_HIT_sum'] / tot:.1f} %")
+        if avg.get("SQ_LDS_BANK_CONFLICT") is not None and avg.get("SQ_LDS_IDX_ACTIVE"):
+            extra.append("LDS bank-conflict cycles per LDS-active cycle, SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: "
+                         f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
+        if extra:
+            lines += [""] + ["- " + e for e in extra]
         lines.append("")
     with open(os.path.join(prof, f"counters_{wl_name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")

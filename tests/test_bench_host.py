@@ -63,8 +63,8 @@ def test_summaries_scale_counters_by_the_copy_kernel(tmp_path):
     # WRITE_SIZE: the copy writes 1,048,576 KiB -> scale 1.0; the kernel 300 KiB
     _run_dir(root, "write", "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --copy-probe-mib 1024", src,
              rows=[(1, FWD, 300.0), (2, FWD, 300.0), (3, COPY, 1048576.0)], counter="WRITE_SIZE")
-    # a counter pass: 32 MFMA per (wave, block) unit, two waves per (tile, block) pair
-    units = PAIRS / (64 * 64) * 2
+    # a counter pass: 32 MFMA per (wave, block) unit, four waves per (tile, block) pair
+    units = PAIRS / (64 * 64) * 4
     _run_dir(root, "counters_1", "rocprofv3 --pmc SQ_INSTS_MFMA -- python3 bench.py", src,
              rows=[(1, FWD, 32 * units), (2, FWD, 32 * units)], counter="SQ_INSTS_MFMA")
     bench.summarize(str(root), prof_dir=str(prof))
