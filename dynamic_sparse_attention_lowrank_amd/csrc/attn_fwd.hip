@@ -27,6 +27,11 @@
 //     are merged once, through LDS, at the end.  Four waves per tile (instead of
 //     fewer, larger ones) keep half as many tiles in flight per XCD, so the
 //     gathered blocks of the tiles that run together fit its L2 better.
+//  2'. attn_fwd_pair (bf16, long sequences): one work-group of 8 waves per pair of
+//     neighbouring query tiles, each tile computed as above by 4 waves, walking the
+//     union of the two kept lists so that a block kept by both is gathered once;
+//     chosen when one head's gathered blocks outgrow the caches (kPairMinHeadBytes),
+//     where the gathers are bound by L2-miss bandwidth.
 // With bf16 inputs the P.V product runs on fp16 matrix cores: v_prep converts
 // V * 2^t, with one power of two per (b, h) that puts the head's largest |v| in
 // [2^14, 2^15) (launch_pow2_scale), so the conversion is exact whatever the size
@@ -485,6 +490,277 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// work-group barrier that orders LDS accesses only: unlike __syncthreads() it does
+// not wait for this wave's global->LDS loads still in flight (the caller waits for
+// exactly the ones it needs first)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): this wave's LDS accesses are done
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::: "memory");
+#endif
+  __builtin_amdgcn_s_barrier();
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::: "memory");
+#endif
+}
+
+// wait until at most N of this wave's vector-memory loads are in flight
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// The kept-block lists of two query tiles walked as one ascending union: each step
+// yields a block and a mask (bit g: tile g kept it), so a block kept by both is
+// loaded once.  Every list element is yielded exactly once whatever the order of
+// the lists (a list that is not ascending only loses sharing), invalid entries are
+// skipped (IdList).  Wave-uniform.
+struct PairMerge {
+  IdList a, b;
+  int ha, hb;                                 // current heads (-1: list done)
+  __device__ __forceinline__ void init(const int* la, const int* lb, int k, int nb, int lane) {
+    a.init(la, k, nb, lane);
+    ha = a.next(lane);
+    if (lb != nullptr) {
+      b.init(lb, k, nb, lane);
+      hb = b.next(lane);
+    } else {
+      hb = -1;
+    }
+  }
+  __device__ __forceinline__ int next(int lane, int& mask) {
+    if (ha < 0 && hb < 0) {
+      mask = 0;
+      return -1;
+    }
+    int blk;
+    if (hb < 0 || (ha >= 0 && ha < hb)) {
+      blk = ha, mask = 1;
+      ha = a.next(lane);
+    } else if (ha < 0 || hb < ha) {
+      blk = hb, mask = 2;
+      hb = b.next(lane);
+    } else {
+      blk = ha, mask = 3;
+      ha = a.next(lane);
+      hb = b.next(lane);
+    }
+    return blk;
+  }
+};
+
+// Which attention kernel a bf16 forward runs: one head's gathered blocks (K rows
+// and the fp16 V^T copy, NB * 64 * d * 4 bytes) below this size stay mostly in the
+// caches, and the one-tile kernel with its deeper per-wave pipeline is faster;
+// above it the gathers are bound by L2-miss bandwidth and the tile-pair kernel,
+// which gathers a block kept by both tiles once, is faster.  Measured crossover at
+// d = 128 (5 % kept, 1x8x8 tiles): NB = 1024 (32 MiB) pair 7 % slower, NB = 1536
+// (48 MiB) 10 % faster, NB = 8192 22 % faster.
+constexpr size_t kPairMinHeadBytes = (size_t)48 << 20;
+
+// bf16 inputs: one work-group of 8 waves per pair of neighbouring query tiles
+// (waves 4g..4g+3 compute tile g exactly as above: wave (qh, kh) takes 32 queries
+// against a 32-key half), one work-group per CU.  The two tiles' kept blocks are
+// walked as one union (PairMerge): a block that both kept -- neighbours along the
+// tile grid's slowest axis keep many of the same blocks -- is gathered once for
+// both, cutting the bytes gathered per attended pair.  The blocks stream through a
+// ring of four LDS slots [K rows | V^T fragments] filled three blocks ahead.
+// Iteration j: wait for block j (blocks j+1, j+2 may stay in flight), barrier (every
+// wave is done with iteration j-1, so its slot is free), request block j+3 into it,
+// and for each tile that kept block j: S = K Q^T, P against the reference maximum,
+// O += V^T P^T.
+template <int D, bool FULL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_pair_kernel(FwdArgs a) {
+  typedef bf16 T;
+  using C = FwdCfg<T, D>;
+  typedef typename C::PT PT;
+  typedef typename Elem<T>::frag Frag;
+  typedef typename Elem<PT>::frag PFrag;
+  using TC = TileCfg<T, D>;
+  constexpr int W = 8;
+  constexpr int NBUF = 4;
+  constexpr int kKB = C::kKBytes, kVB = C::kVBytes, kSlot = kKB + kVB;
+  constexpr int kVInstr = kVB / 1024 / W;                      // 1 KB direct loads per wave and block (V)
+  constexpr int kDmaPerWave = DmaCfg<T, D, W>::kPer + kVInstr;
+  static_assert(kVB % (1024 * W) == 0, "V^T block splits evenly over the waves");
+  constexpr int kHalfT = C::kDTiles / 2 > 0 ? C::kDTiles / 2 : 1;
+  constexpr int kMrgFloats = kHalfT * 16 * 64 + 2 * 64;
+  static_assert(W * kMrgFloats * 4 <= NBUF * kSlot, "merge area fits the ring");
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * kSlot];
+
+  const Geo g = a.g;
+  const int L = blockIdx.x;                 // natural order: neighbouring pairs of one head
+  const int bh = L / a.npairs;
+  const int pi = L - bh * a.npairs;
+  // pair pi -> tiles tau0 = (outer * E + 2p) * S + r and tau0 + S (if 2p + 1 < E)
+  const int r = pi % a.pair_s, qo = pi / a.pair_s;
+  const int pp = qo % a.pair_p2, outer = qo / a.pair_p2;
+  const int tau0 = (outer * a.pair_e + 2 * pp) * a.pair_s + r;
+  const int tau1 = 2 * pp + 1 < a.pair_e ? tau0 + a.pair_s : -1;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int grp = w >> 2, qh = w & 1, kh = (w >> 1) & 1;
+  const int tau = grp == 0 ? tau0 : tau1;
+  const bool active = tau >= 0;
+
+  const size_t head_off = (size_t)bh * g.N * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(a.Q) + head_off;
+  const int* __restrict__ ibase = a.idx + (size_t)bh * g.NB * a.kmax;
+  int kk = a.kvec[bh];
+  kk = kk < 1 ? 1 : (kk > a.kmax ? a.kmax : kk);
+
+  // this lane's query (column l%32 of S^T) of its group's tile: Q^T B-fragments
+  const int qr = 32 * qh + l32;
+  const bool q_ok = active && qr < g.T;
+  const int q_tok = (active ? tile_base(g, tau) : 0) + (q_ok ? member_offset(g, qr) : 0);
+  Frag qf[C::kSteps];
+  {
+    const T* qrow = Qh + (size_t)q_tok * D;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      u32x4 ch[C::kFC];
+#pragma unroll
+      for (int p = 0; p < C::kFC; ++p)
+        ch[p] = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * h + TC::kCE * p) : u32x4{0, 0, 0, 0};
+      qf[s] = frag_from_chunks(ch, (T*)nullptr);
+    }
+  }
+
+  const int kvalid = g.T - 32 * kh;           // valid keys in this wave's half (may be <= 0)
+  WaveState<T, D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int t = 0; t < C::kDTiles; ++t) st.o[t] = f32x16{};
+
+  int koff[DmaCfg<T, D, W>::kPer];
+  dma_offsets<T, D, W>(koff, g, w, lane);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(reinterpret_cast<const T*>(a.K) + head_off, (size_t)g.N * D * sizeof(T));
+  const size_t hblk = (size_t)g.NB * 64 * D;
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(reinterpret_cast<const PT*>(a.Vt) + (size_t)bh * hblk, hblk * sizeof(PT));
+  auto request = [&](int blk, int slot) {
+    char* b = smem + slot * kSlot;
+    dma_tile<T, D, W>(reinterpret_cast<u32x4*>(b), rk, tile_base(g, blk) * D * (int)sizeof(T), koff, w);
+    dma_linear<kVInstr, W>(reinterpret_cast<u32x4*>(b + kKB), rv, blk * kVB, w, lane);
+  };
+  const float c2 = a.c;
+
+  PairMerge mg;
+  mg.init(ibase + (size_t)tau0 * a.kmax, tau1 >= 0 ? ibase + (size_t)tau1 * a.kmax : nullptr, kk, g.NB, lane);
+  int blk[NBUF], msk[NBUF];                   // entries j .. j+NBUF-1 of the union
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) blk[i] = -1, msk[i] = 0;
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) {
+    if (i == 0 || blk[i - 1] >= 0) blk[i] = mg.next(lane, msk[i]);
+    if (blk[i] >= 0) request(blk[i], i);
+  }
+  int slot = 0;
+  while (blk[0] >= 0) {
+    // block j landed; blocks j+1, j+2 may still be in flight
+    if (blk[2] >= 0) vm_wait<2 * kDmaPerWave>();
+    else if (blk[1] >= 0) vm_wait<kDmaPerWave>();
+    else dma_wait();
+    lds_barrier();                            // iteration j-1 done everywhere: its slot is free
+    if (blk[2] >= 0) blk[3] = mg.next(lane, msk[3]);
+    else blk[3] = -1, msk[3] = 0;
+    if (blk[3] >= 0) request(blk[3], slot == 0 ? NBUF - 1 : slot - 1);
+    if (active && ((msk[0] >> grp) & 1) && kvalid > 0) {
+      const u32x4* lk = reinterpret_cast<const u32x4*>(smem + slot * kSlot);
+      const u32x4* lv = reinterpret_cast<const u32x4*>(smem + slot * kSlot + kKB) + (size_t)kh * C::kVFrag * 64 + lane;
+      Frag kf[C::kSteps];
+#pragma unroll
+      for (int k = 0; k < C::kSteps; ++k) kf[k] = frag_row<T, D>(lk, 32 * kh + l32, k, h);
+      PFrag vf[C::kDTiles][2];
+#pragma unroll
+      for (int t = 0; t < C::kDTiles; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4 ch[C::kPFC];
+#pragma unroll
+          for (int p = 0; p < C::kPFC; ++p) ch[p] = lv[((t * 2 + ks) * C::kPFC + p) * 64];
+          vf[t][ks] = frag_from_chunks(ch, (PT*)nullptr);
+        }
+      }
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int k = 0; k < C::kSteps; ++k) sc = mma_step(kf[k], qf[k], sc);
+      PFrag pf[2];
+      float bs = block_probs<T, D, FULL>(st, sc, pf, c2, kvalid, h);
+      if (ballot(!(bs < kSumBound))) {        // rare: raise the reference maximum first
+        raise_max(st, sc, c2);
+        bs = block_probs<T, D, FULL>(st, sc, pf, c2, kvalid, h);
+      }
+      st.l += bs;
+#pragma unroll
+      for (int t = 0; t < C::kDTiles; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) st.o[t] = mma_step(vf[t][ks], pf[ks], st.o[t]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) blk[i] = blk[i + 1], msk[i] = msk[i + 1];
+    slot = slot == NBUF - 1 ? 0 : slot + 1;
+  }
+  __syncthreads();                            // the ring is free: reuse it for the merge
+
+  // ---- merge the two key halves of each query half (partner: the other kh of the group)
+  float* mrg = reinterpret_cast<float*>(smem);
+  float* mine = mrg + w * kMrgFloats;
+  const float* theirs = mrg + (w ^ 2) * kMrgFloats;
+  const int t0 = C::kDTiles >= 2 ? kh * kHalfT : 0;
+  const int o0 = C::kDTiles >= 2 ? (1 - kh) * kHalfT : 0;
+#pragma unroll
+  for (int t = 0; t < kHalfT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = st.o[0][i];
+#pragma unroll
+      for (int u = 0; u < C::kDTiles; ++u)
+        if (u == o0 + t) v = st.o[u][i];
+      mine[(t * 16 + i) * 64 + lane] = v;
+    }
+  }
+  mine[kHalfT * 16 * 64 + lane] = st.m;
+  mine[kHalfT * 16 * 64 + 64 + lane] = st.l;
+  __syncthreads();
+  const float ma = st.m, la = pair_sum(st.l);
+  const float mb = theirs[kHalfT * 16 * 64 + lane];
+  const float lb = pair_sum(theirs[kHalfT * 16 * 64 + 64 + lane]);
+  const float mt = fmaxf(ma, mb);
+  const float wa = (ma == -INFINITY) ? 0.f : fast_exp2(ma - mt);
+  const float wb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - mt);
+  const float l_tot = wa * la + wb * lb;
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  inv *= a.vscale[bh].y;                      // undo the fp16 copy's 2^t (exact)
+  if (q_ok) {
+    const size_t orow = head_off + (size_t)q_tok * D;
+#pragma unroll
+    for (int t = 0; t < kHalfT; ++t) {
+      const int td = t0 + t;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * gq + i;
+          float own = st.o[0][rr];
+#pragma unroll
+          for (int u = 0; u < C::kDTiles; ++u)
+            if (u == td) own = st.o[u][rr];
+          v[i] = (wa * own + wb * theirs[(t * 16 + rr) * 64 + lane]) * inv;
+        }
+        store4(a.O, orow + 32 * td + 8 * gq + 4 * h, a.out_f32, v[0], v[1], v[2], v[3]);
+      }
+    }
+    if (kh == 0 && h == 0) a.LSE[(size_t)bh * g.N + q_tok] = l_tot > 0.f ? (mt + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
   typedef typename PVType<T>::type PT;
@@ -497,6 +773,22 @@ hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
     const hipError_t e = launch_pow2_scale(a.V, a.BH, (size_t)a.g.N * D, a.vmax, a.vscale, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v_prep16_kernel<D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
+    const Geo& g = a.g;
+    if ((size_t)g.NB * 64 * D * 4 < kPairMinHeadBytes) {
+      if (g.T == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(a.BH * g.NB), dim3(kFwdThreads), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(a.BH * g.NB), dim3(kFwdThreads), 0, s, a);
+      return hipGetLastError();
+    }
+    // pairs of tiles along the slowest tile-grid axis with more than one tile
+    if (g.gt > 1) a.pair_s = g.gh * g.gw, a.pair_e = g.gt;
+    else if (g.gh > 1) a.pair_s = g.gw, a.pair_e = g.gh;
+    else a.pair_s = 1, a.pair_e = g.gw;
+    a.pair_p2 = (a.pair_e + 1) / 2;
+    a.npairs = g.NB / a.pair_e * a.pair_p2;
+    const dim3 grid((unsigned)(a.BH * a.npairs));
+    if (g.T == 64) hipLaunchKernelGGL((attn_fwd_pair_kernel<D, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_pair_kernel<D, false>), grid, dim3(512), 0, s, a);
+    return hipGetLastError();
   } else {
     hipLaunchKernelGGL((v_prep_kernel<T, D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
   }

@@ -27,6 +27,10 @@ struct FwdArgs {
   float2* vscale;   // workspace [BH]: (2^t, 2^-t), the fp16 V copy's power-of-two scale
   Geo g;
   int BH;
+  // query-tile pairs (bf16 forward): tiles tau and tau + pair_s, neighbours along
+  // one axis of the tile grid (extent pair_e, pair_p2 = ceil(pair_e / 2) pairs per
+  // line); npairs pairs per head
+  int pair_s, pair_e, pair_p2, npairs;
 };
 size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32);
 hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s);
