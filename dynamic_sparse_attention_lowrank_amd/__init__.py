@@ -27,10 +27,12 @@ __all__ = [
     "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
     "bwd_workspace_bytes", "fwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
     "predict_select", "predictor_grad", "predictor_grad_workspace_bytes", "rope3d",
+    "set_fwd_kernel", "get_fwd_kernel", "FWD_AUTO", "FWD_ONE_TILE", "FWD_TILE_PAIR",
 ]
 
 F32 = 0
 BF16 = 1
+FWD_AUTO, FWD_ONE_TILE, FWD_TILE_PAIR = 0, 1, 2
 _LIB_NAME = "libdsa.so"
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 
@@ -71,6 +73,10 @@ def _load():
     L.dsa_rope3d.argtypes = [sp, i32, f32, i32, i32, i32, i32, vp, vp, vp]
     L.dsa_attn_fwd.restype = ctypes.c_int
     L.dsa_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+    L.dsa_set_fwd_kernel.restype = ctypes.c_int
+    L.dsa_set_fwd_kernel.argtypes = [i32]
+    L.dsa_get_fwd_kernel.restype = i32
+    L.dsa_get_fwd_kernel.argtypes = []
     L.dsa_attn_fwd_noalloc.restype = ctypes.c_int
     L.dsa_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp]
     L.dsa_attn_fwd_workspace_bytes.restype = sz
@@ -362,6 +368,16 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tenso
                              _io_code(O), _ptr(O), _ptr(LSE), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream()))
     return O, LSE
+
+
+def set_fwd_kernel(kind: int) -> None:
+    """Which bf16 forward kernel runs: FWD_AUTO (by size), FWD_ONE_TILE or
+    FWD_TILE_PAIR (process-wide; see dsa_set_fwd_kernel in include/dsa.h)."""
+    _check(_L().dsa_set_fwd_kernel(int(kind)))
+
+
+def get_fwd_kernel() -> int:
+    return int(_L().dsa_get_fwd_kernel())
 
 
 def attn_fwd_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, k: torch.Tensor,

@@ -9,6 +9,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -114,6 +115,9 @@ bool csc_fits(const Derived& dv, int kmax) { return (int64_t)dv.g.NB * kmax <= (
 // unscaled scores)
 bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
+// bf16 forward kernel choice (dsa_set_fwd_kernel), read at every forward call
+std::atomic<int32_t> g_fwd_kernel{DSA_FWD_AUTO};
+
 // --- fixed scratch of dsa_attn_fwd_noalloc ------------------------------------
 // One array per GPU (each device that loads this code object holds its own copy,
 // at its own address).  In host code `fwd_scratch` only names the symbol: its
@@ -161,11 +165,20 @@ const char* dsa_status_string(dsa_status s) {
     case DSA_ERR_RANK: return "DSA_ERR_RANK: predictor rank must be in [1, 64]";
     case DSA_ERR_SCRATCH:
       return "DSA_ERR_SCRATCH: one head's forward workspace exceeds the 144 MiB scratch of dsa_attn_fwd_noalloc";
+    case DSA_ERR_ARG: return "DSA_ERR_ARG: an enumerated argument is out of range";
   }
   return "unknown dsa_status";
 }
 
 int32_t dsa_version(void) { return 200; }
+
+dsa_status dsa_set_fwd_kernel(int32_t kind) {
+  if (kind != DSA_FWD_AUTO && kind != DSA_FWD_ONE_TILE && kind != DSA_FWD_TILE_PAIR) return DSA_ERR_ARG;
+  g_fwd_kernel.store(kind, std::memory_order_relaxed);
+  return DSA_OK;
+}
+
+int32_t dsa_get_fwd_kernel(void) { return g_fwd_kernel.load(std::memory_order_relaxed); }
 
 dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q, const void* K, const void* Wq,
                        const void* Wk, float* Qbar, float* Kbar, float* S, hipStream_t stream) {
@@ -295,6 +308,7 @@ dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const void* K, co
   a.c = scale * kLog2e;
   a.Vt = workspace;
   a.g = dv.g; a.BH = dv.BH;
+  a.kernel = g_fwd_kernel.load(std::memory_order_relaxed);
   return hip_status(launch_attn_fwd(a, dv.io_f32, dv.d, stream));
 }
 
@@ -333,6 +347,7 @@ dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, const voi
     a.out_f32 = out_dtype == DSA_F32;
     a.c = scale * kLog2e;
     a.Vt = ws;
+    a.kernel = g_fwd_kernel.load(std::memory_order_relaxed);
     a.g = dv.g;
     a.BH = std::min(G, dv.BH - h0);
     st = hip_status(launch_attn_fwd(a, dv.io_f32, dv.d, stream));

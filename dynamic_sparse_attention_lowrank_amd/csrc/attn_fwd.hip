@@ -774,7 +774,8 @@ hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v_prep16_kernel<D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
     const Geo& g = a.g;
-    if ((size_t)g.NB * 64 * D * 4 < kPairMinHeadBytes) {
+    const bool pair = a.kernel == 2 || (a.kernel == 0 && (size_t)g.NB * 64 * D * 4 >= kPairMinHeadBytes);
+    if (!pair) {
       if (g.T == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(a.BH * g.NB), dim3(kFwdThreads), 0, s, a);
       else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(a.BH * g.NB), dim3(kFwdThreads), 0, s, a);
       return hipGetLastError();

@@ -31,6 +31,7 @@ struct FwdArgs {
   // one axis of the tile grid (extent pair_e, pair_p2 = ceil(pair_e / 2) pairs per
   // line); npairs pairs per head
   int pair_s, pair_e, pair_p2, npairs;
+  int kernel;   // bf16 forward kernel: 0 by size, 1 one-tile, 2 tile-pair
 };
 size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32);
 hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s);

@@ -68,8 +68,9 @@ typedef enum {
   DSA_ERR_HIP = 7,             /* a HIP launch failed                              */
   DSA_ERR_NOT_IMPLEMENTED = 8, /* combination not supported by this build          */
   DSA_ERR_RANK = 9,            /* predictor rank r out of range                    */
-  DSA_ERR_SCRATCH = 10         /* one head needs more than dsa_attn_fwd_noalloc's
+  DSA_ERR_SCRATCH = 10,        /* one head needs more than dsa_attn_fwd_noalloc's
                                   fixed device scratch                             */
+  DSA_ERR_ARG = 11             /* an enumerated argument is out of range           */
 } dsa_status;
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
@@ -225,6 +226,26 @@ DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const voi
                                 const int32_t* idx, const int32_t* k, int32_t kmax, float scale,
                                 int32_t out_dtype, void* O, float* LSE, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_set_fwd_kernel / dsa_get_fwd_kernel -- which kernel the bf16 forward
+ *   (dsa_attn_fwd, dsa_attn_fwd_noalloc) runs.  Both compute the same function
+ *   (the DSV page, section 4, stage two) to the same precision, in different
+ *   orders of summation, so O and LSE may differ in the last bits between them:
+ *     DSA_FWD_ONE_TILE:  one work-group per query tile, its kept blocks gathered
+ *                        for it alone;
+ *     DSA_FWD_TILE_PAIR: one work-group per two neighbouring query tiles, walking
+ *                        the union of their kept blocks, so that a block both kept
+ *                        is gathered once;
+ *     DSA_FWD_AUTO (the default): the tile-pair kernel when one head's gathered
+ *                        blocks (NB * 64 * d * 4 bytes) reach 48 MiB, where the
+ *                        gathers run at L2-miss bandwidth, else the one-tile kernel.
+ *   fp32 io always runs its one kernel.  The setting is process-wide, read at each
+ *   forward call; an unknown kind returns DSA_ERR_ARG and changes nothing.
+ */
+typedef enum { DSA_FWD_AUTO = 0, DSA_FWD_ONE_TILE = 1, DSA_FWD_TILE_PAIR = 2 } dsa_fwd_kernel;
+DSA_API dsa_status dsa_set_fwd_kernel(int32_t kind);
+DSA_API int32_t dsa_get_fwd_kernel(void);
 
 /*
  * dsa_attn_fwd_noalloc -- dsa_attn_fwd for callers that cannot allocate device

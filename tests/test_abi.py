@@ -214,3 +214,23 @@ def test_workspace_formula(L):
 def test_status_strings(L):
     for code in range(10):
         assert L.lib.dsa_status_string(code).startswith(b"DSA_")
+
+
+def test_fwd_kernel_choice(L):
+    """dsa_set_fwd_kernel takes the three kinds and rejects others (DSA_ERR_ARG),
+    leaving the setting unchanged; no device call is made."""
+    lib = L.lib
+    assert lib.dsa_get_fwd_kernel() == 0
+    try:
+        for kind in (1, 2, 0):
+            assert lib.dsa_set_fwd_kernel(kind) == 0
+            assert lib.dsa_get_fwd_kernel() == kind
+        lib.dsa_set_fwd_kernel(2)
+        for bad in (-1, 3, 1 << 30):
+            assert lib.dsa_set_fwd_kernel(bad) == 11
+            assert lib.dsa_get_fwd_kernel() == 2
+        with pytest.raises(L.DsaError):
+            L.set_fwd_kernel(5)
+    finally:
+        lib.dsa_set_fwd_kernel(0)
+    assert L.get_fwd_kernel() == L.FWD_AUTO
