@@ -22,15 +22,29 @@ namespace dsa {
 
 namespace {
 
+// largest bf16 magnitude pattern among the 8 values of a 16-byte chunk
+__device__ __forceinline__ uint32_t chunk_absmax(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max(v[e] & 0x7fffu, (v[e] >> 16) & 0x7fffu));
+  return m;
+}
+
+// grid-stride over the chunks of one head, four loads in flight per thread
 __global__ __launch_bounds__(256) void absmax_kernel(const void* X, size_t chunks16, uint32_t* partial) {
   const int bh = blockIdx.x / kDoChunks, c = blockIdx.x - bh * kDoChunks;
   const u32x4* __restrict__ p = reinterpret_cast<const u32x4*>(X) + (size_t)bh * chunks16;
+  constexpr size_t kStride = (size_t)kDoChunks * 256;
   uint32_t m = 0;
-  for (size_t i = (size_t)c * 256 + threadIdx.x; i < chunks16; i += (size_t)kDoChunks * 256) {
-    const u32x4 v = p[i];
+  size_t i = (size_t)c * 256 + threadIdx.x;
+  for (; i + 3 * kStride < chunks16; i += 4 * kStride) {
+    u32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) m = max(m, max(v[e] & 0x7fffu, (v[e] >> 16) & 0x7fffu));
+    for (int u = 0; u < 4; ++u) v[u] = p[i + u * kStride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = max(m, chunk_absmax(v[u]));
   }
+  for (; i < chunks16; i += kStride) m = max(m, chunk_absmax(p[i]));
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
   __shared__ uint32_t wm[4];
