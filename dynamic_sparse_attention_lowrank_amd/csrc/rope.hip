@@ -10,10 +10,12 @@
 // dtype, are what the predictor and the attention read); the inverse rotation
 // maps the gradients of the rotated tensors back.
 //
-// Kernel: one thread per (token, pair): its angle, sine and cosine are computed
-// once (fp32, accurate sincosf) and applied to that pair in every (b, h) row; a
-// wave covers one 256-byte token row (d = 128, bf16) per (b, h), so every load and
-// store is coalesced.  HBM-bound: reads and writes the tensor once.
+// Kernel: one thread per 16-byte chunk of a token row (4 bf16 or 2 fp32 pairs):
+// the angles, sines and cosines of its pairs are computed once (fp32, accurate
+// sincosf) and applied to those pairs in every (b, h) row, so every load and store
+// is a full 16 bytes per lane and coalesced.  HBM-bound: reads and writes the
+// tensor once.  Tensors that are only pair-aligned (a view at an odd offset) take
+// the same arithmetic one pair per thread.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,14 +50,10 @@ struct Pair2<float> {
   static __device__ __forceinline__ raw put(float u, float v) { return make_float2(u, v); }
 };
 
-template <typename T>
-__global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a) {
-  typedef typename Pair2<T>::raw raw;
-  const Geo g = a.g;
+// sine and cosine of the rotation of pair p of token n
+__device__ __forceinline__ void pair_angle(const RopeArgs& a, int n, int p, float& sn, float& cs) {
+  const Geo& g = a.g;
   const int pairs = a.d / 2;
-  const long long i = (long long)blockIdx.x * kRopeThreads + threadIdx.x;
-  if (i >= (long long)g.N * pairs) return;
-  const int n = (int)(i / pairs), p = (int)(i - (long long)n * pairs);
   // section of pair p and its index inside the section
   const int m_t = pairs - 2 * (pairs / 3), m_s = pairs / 3;
   int axis, li, m;
@@ -69,9 +67,61 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a) {
   const int plane = g.Lh * g.Lw;
   const int pos = axis == 0 ? n / plane + a.t0 : (axis == 1 ? (n / g.Lw) % g.Lh + a.y0 : n % g.Lw + a.x0);
   const float freq = exp2f(-(float)(2 * li) / (float)(2 * m) * a.log2_base);
-  float sn, cs;
   sincosf((float)pos * freq, &sn, &cs);
   if (a.inverse) sn = -sn;
+}
+
+// 16-byte chunks: P pairs per thread (both tensors 16-byte aligned)
+template <typename T>
+__global__ __launch_bounds__(kRopeThreads) void rope3d_chunk_kernel(RopeArgs a) {
+  typedef typename Pair2<T>::raw raw;
+  constexpr int P = 16 / (int)sizeof(raw);
+  const int cpr = a.d / 2 / P;                 // chunks per token row
+  const long long i = (long long)blockIdx.x * kRopeThreads + threadIdx.x;
+  if (i >= (long long)a.g.N * cpr) return;
+  const int n = (int)(i / cpr), c = (int)(i - (long long)n * cpr);
+  float sn[P], cs[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) pair_angle(a, n, c * P + e, sn[e], cs[e]);
+
+  const u32x4* __restrict__ X = reinterpret_cast<const u32x4*>(a.X);
+  u32x4* __restrict__ Y = reinterpret_cast<u32x4*>(a.Y);
+  const size_t row = (size_t)a.g.N * cpr;      // chunks per (b, h)
+  for (int b0 = 0; b0 < a.BH; b0 += kRopeUnroll) {
+    u32x4 v[kRopeUnroll];
+#pragma unroll
+    for (int u = 0; u < kRopeUnroll; ++u)
+      if (b0 + u < a.BH) v[u] = X[(size_t)(b0 + u) * row + i];
+#pragma unroll
+    for (int u = 0; u < kRopeUnroll; ++u) {
+      if (b0 + u < a.BH) {
+        raw r[P];
+        __builtin_memcpy(r, &v[u], 16);
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          float x0, x1;
+          Pair2<T>::get(r[e], x0, x1);
+          r[e] = Pair2<T>::put(fmaf(x0, cs[e], -x1 * sn[e]), fmaf(x0, sn[e], x1 * cs[e]));
+        }
+        u32x4 o;
+        __builtin_memcpy(&o, r, 16);
+        Y[(size_t)(b0 + u) * row + i] = o;
+      }
+    }
+  }
+}
+
+// one pair per thread (tensors aligned to a pair only)
+template <typename T>
+__global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a) {
+  typedef typename Pair2<T>::raw raw;
+  const Geo g = a.g;
+  const int pairs = a.d / 2;
+  const long long i = (long long)blockIdx.x * kRopeThreads + threadIdx.x;
+  if (i >= (long long)g.N * pairs) return;
+  const int n = (int)(i / pairs), p = (int)(i - (long long)n * pairs);
+  float sn, cs;
+  pair_angle(a, n, p, sn, cs);
 
   const raw* __restrict__ X = reinterpret_cast<const raw*>(a.X);
   raw* __restrict__ Y = reinterpret_cast<raw*>(a.Y);
@@ -95,6 +145,15 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(RopeArgs a) {
 }  // namespace
 
 hipError_t launch_rope3d(const RopeArgs& a, int f32, hipStream_t s) {
+  if ((((uintptr_t)a.X | (uintptr_t)a.Y) & 15u) == 0) {
+    const long long work = (long long)a.g.N * (a.d / 2) / (f32 ? 2 : 4);
+    const unsigned grid = (unsigned)((work + kRopeThreads - 1) / kRopeThreads);
+    if (f32)
+      hipLaunchKernelGGL((rope3d_chunk_kernel<float>), dim3(grid), dim3(kRopeThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((rope3d_chunk_kernel<bf16>), dim3(grid), dim3(kRopeThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const long long work = (long long)a.g.N * (a.d / 2);
   const unsigned grid = (unsigned)((work + kRopeThreads - 1) / kRopeThreads);
   if (f32)
