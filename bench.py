@@ -431,7 +431,8 @@ def main():
     # dominant single-kernel phase and its algorithmic work per launch: forward 4*d
     # per pair; dK/dV 8*d (S, dP, dV, dK); dQ 2*d (dQ only: its recomputation of S
     # and dP is extra work, not algorithmic)
-    algo = {"fwd": (4.0 * d * pairs, "attn_fwd_kernel")}
+    fwd_kernel = "attn_fwd_pair_kernel" if dsa.fwd_kernel_for(Q, lay) == dsa.FWD_TILE_PAIR else "attn_fwd_kernel"
+    algo = {"fwd": (4.0 * d * pairs, fwd_kernel)}
     if train:
         algo.update({"bwd_dkdv": (8.0 * d * pairs, "bwd_dkdv_kernel"), "bwd_dq": (2.0 * d * pairs, "bwd_dq_kernel")})
     dom = max(algo, key=lambda p: phase_ms[p])
@@ -667,12 +668,12 @@ def summarize(root: str, prof_dir: Optional[str] = None):
 # (forward), one wave's 16 keys against one query tile (dK/dV) or its 16 queries
 # against one kept block (dQ): four waves share each (query tile, kept block) pair
 # in every kernel -- so that instruction mixes and unit busy times compare
-_UNITS = {"attn_fwd_kernel": 4, "bwd_dkdv_kernel": 4, "bwd_dq_kernel": 4}
+_UNITS = {"attn_fwd_kernel": 4, "attn_fwd_pair_kernel": 4, "bwd_dkdv_kernel": 4, "bwd_dq_kernel": 4}
 
 
 def summarize_counters(root: str, wl_name: str, src_hash: str, prof: str):
     """profiles/counters_<workload>.md from the --pmc runs under DIR/counters_* (each
-    with cmd.txt and out.json like the traffic runs), for the three attention kernels."""
+    with cmd.txt and out.json like the traffic runs), for the attention kernels."""
     import glob
     subs = sorted(glob.glob(os.path.join(root, "counters_*")))
     if not subs:

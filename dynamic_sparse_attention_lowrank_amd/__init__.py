@@ -27,7 +27,7 @@ __all__ = [
     "Layout", "lib", "library_path", "predict", "select", "attn_fwd", "attn_bwd",
     "bwd_workspace_bytes", "fwd_workspace_bytes", "attn_bwd_prepare", "attn_bwd_dkdv", "attn_bwd_dq", "DsaError", "F32", "BF16",
     "predict_select", "predictor_grad", "predictor_grad_workspace_bytes", "rope3d",
-    "set_fwd_kernel", "get_fwd_kernel", "FWD_AUTO", "FWD_ONE_TILE", "FWD_TILE_PAIR",
+    "set_fwd_kernel", "get_fwd_kernel", "fwd_kernel_for", "FWD_AUTO", "FWD_ONE_TILE", "FWD_TILE_PAIR",
 ]
 
 F32 = 0
@@ -77,6 +77,8 @@ def _load():
     L.dsa_set_fwd_kernel.argtypes = [i32]
     L.dsa_get_fwd_kernel.restype = i32
     L.dsa_get_fwd_kernel.argtypes = []
+    L.dsa_fwd_kernel_for.restype = i32
+    L.dsa_fwd_kernel_for.argtypes = [sp]
     L.dsa_attn_fwd_noalloc.restype = ctypes.c_int
     L.dsa_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, vp]
     L.dsa_attn_fwd_workspace_bytes.restype = sz
@@ -378,6 +380,15 @@ def set_fwd_kernel(kind: int) -> None:
 
 def get_fwd_kernel() -> int:
     return int(_L().dsa_get_fwd_kernel())
+
+
+def fwd_kernel_for(Q: torch.Tensor, layout: Layout) -> int:
+    """FWD_ONE_TILE or FWD_TILE_PAIR: the kernel attn_fwd runs for Q's shape now."""
+    sh = _shape(Q, layout)
+    r = int(_L().dsa_fwd_kernel_for(ctypes.byref(sh)))
+    if r < 0:
+        raise ValueError("invalid shape for the forward")
+    return r
 
 
 def attn_fwd_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, k: torch.Tensor,

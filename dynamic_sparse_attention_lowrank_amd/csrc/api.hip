@@ -180,6 +180,12 @@ dsa_status dsa_set_fwd_kernel(int32_t kind) {
 
 int32_t dsa_get_fwd_kernel(void) { return g_fwd_kernel.load(std::memory_order_relaxed); }
 
+int32_t dsa_fwd_kernel_for(const dsa_shape* shape) {
+  Derived dv;
+  if (derive(shape, &dv) != DSA_OK) return -1;
+  return attn_fwd_kernel_for(dv.g, dv.d, dv.io_f32, g_fwd_kernel.load(std::memory_order_relaxed));
+}
+
 dsa_status dsa_predict(const dsa_shape* shape, int32_t r, const void* Q, const void* K, const void* Wq,
                        const void* Wk, float* Qbar, float* Kbar, float* S, hipStream_t stream) {
   Derived dv;

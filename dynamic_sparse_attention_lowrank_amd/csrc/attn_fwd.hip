@@ -774,8 +774,7 @@ hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v_prep16_kernel<D>), dim3(a.BH * a.g.NB), dim3(256), 0, s, a);
     const Geo& g = a.g;
-    const bool pair = a.kernel == 2 || (a.kernel == 0 && (size_t)g.NB * 64 * D * 4 >= kPairMinHeadBytes);
-    if (!pair) {
+    if (attn_fwd_kernel_for(g, D, 0, a.kernel) == 1) {
       if (g.T == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(a.BH * g.NB), dim3(kFwdThreads), 0, s, a);
       else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(a.BH * g.NB), dim3(kFwdThreads), 0, s, a);
       return hipGetLastError();
@@ -799,6 +798,12 @@ hipError_t launch_fwd(const FwdArgs& a0, hipStream_t s) {
 }
 
 }  // namespace
+
+int attn_fwd_kernel_for(const Geo& g, int d, int io_f32, int setting) {
+  if (io_f32) return 1;
+  if (setting == 1 || setting == 2) return setting;
+  return (size_t)g.NB * 64 * d * 4 >= kPairMinHeadBytes ? 2 : 1;
+}
 
 size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32) {
   const size_t copy = (size_t)BH * NB * d * 64 * (io_f32 ? 4 : 2);       // V^T, fragment-major

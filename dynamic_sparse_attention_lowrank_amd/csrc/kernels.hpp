@@ -34,6 +34,8 @@ struct FwdArgs {
   int kernel;   // bf16 forward kernel: 0 by size, 1 one-tile, 2 tile-pair
 };
 size_t attn_fwd_workspace_bytes(int BH, int NB, int d, int io_f32);
+// forward kernel a shape runs: 1 one-tile, 2 tile-pair (setting: 0 by size, 1, 2)
+int attn_fwd_kernel_for(const Geo& g, int d, int io_f32, int setting);
 hipError_t launch_attn_fwd(const FwdArgs& a, int io_f32, int d, hipStream_t s);
 
 struct PredictArgs {

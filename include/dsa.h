@@ -246,6 +246,9 @@ DSA_API dsa_status dsa_attn_fwd(const dsa_shape* shape, const void* Q, const voi
 typedef enum { DSA_FWD_AUTO = 0, DSA_FWD_ONE_TILE = 1, DSA_FWD_TILE_PAIR = 2 } dsa_fwd_kernel;
 DSA_API dsa_status dsa_set_fwd_kernel(int32_t kind);
 DSA_API int32_t dsa_get_fwd_kernel(void);
+/* The kernel a forward of this shape runs under the current setting:
+ * DSA_FWD_ONE_TILE or DSA_FWD_TILE_PAIR; -1 for an invalid shape.  Host only. */
+DSA_API int32_t dsa_fwd_kernel_for(const dsa_shape* shape);
 
 /*
  * dsa_attn_fwd_noalloc -- dsa_attn_fwd for callers that cannot allocate device

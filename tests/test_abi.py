@@ -234,3 +234,25 @@ def test_fwd_kernel_choice(L):
     finally:
         lib.dsa_set_fwd_kernel(0)
     assert L.get_fwd_kernel() == L.FWD_AUTO
+
+
+def test_fwd_kernel_for_shape(L):
+    """The size rule (bf16: tile-pair once one head's gathered blocks, NB*64*d*4
+    bytes, reach 48 MiB), the forced settings, fp32 (always one-tile) and invalid
+    shapes (-1)."""
+    lib = L.lib
+    f = lambda **kw: lib.dsa_fwd_kernel_for(ctypes.byref(_shape(L, **kw)))
+    bf = dict(d=128, tt=1, th=8, tw=8, io=1)
+    assert f(Lt=16, Lh=32, Lw=64, **bf) == 1                 # 512 blocks: 16 MiB
+    assert f(Lt=24, Lh=32, Lw=64, **bf) == 1                 # 768 blocks: 24 MiB
+    assert f(Lt=48, Lh=32, Lw=64, **bf) == 2                 # 1536 blocks: 48 MiB
+    assert f(Lt=32, Lh=128, Lw=128, **bf) == 2               # 8192 blocks
+    assert f(Lt=32, Lh=128, Lw=128, d=128, tt=1, th=8, tw=8, io=0) == 1
+    assert f(Lt=16, Lh=32, Lw=64, d=96, tt=1, th=8, tw=8, io=1) == -1
+    try:
+        lib.dsa_set_fwd_kernel(2)
+        assert f(Lt=16, Lh=32, Lw=64, **bf) == 2
+        lib.dsa_set_fwd_kernel(1)
+        assert f(Lt=32, Lh=128, Lw=128, **bf) == 1
+    finally:
+        lib.dsa_set_fwd_kernel(0)
