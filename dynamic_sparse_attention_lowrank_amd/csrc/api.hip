@@ -68,7 +68,7 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t dvec, bitmap, counts, offsets, entries, do16, dmax, dscale, vmax, vscale;
+  size_t dvec, bitmap, counts, offsets, entries, order, do16, dmax, dscale, vmax, vscale;
   size_t dabs, dabs_part, du, q16, qmax, qscale, k16, kmaxp, kscale, vmax_q, vscale_q, total;
   int words;
 };
@@ -83,6 +83,7 @@ BwdLayout bwd_layout(const Derived& dv, int kmax) {
   l.counts = off;  off += align256(BH * NB * sizeof(int32_t));
   l.offsets = off; off += align256(BH * (NB + 1) * sizeof(int32_t));
   l.entries = off; off += align256(BH * NB * (size_t)kmax * sizeof(int32_t));
+  l.order = off;   off += align256(BH * NB * sizeof(int32_t));
   l.do16 = off;    off += dv.io_f32 ? 0 : align256(BH * N * (size_t)dv.d * 2);
   l.dmax = off;    off += dv.io_f32 ? 0 : align256(BH * kDoChunks * sizeof(uint32_t));
   l.dscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
@@ -405,6 +406,7 @@ dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const v
   a.counts = reinterpret_cast<int32_t*>(ws + l.counts);
   a.offsets = reinterpret_cast<int32_t*>(ws + l.offsets);
   a.entries = reinterpret_cast<int32_t*>(ws + l.entries);
+  a.order = dv.g.NB <= kOrderMaxNB ? reinterpret_cast<int32_t*>(ws + l.order) : nullptr;
   a.dO16 = dv.io_f32 ? nullptr : ws + l.do16;
   a.dmax = dv.io_f32 ? nullptr : reinterpret_cast<uint32_t*>(ws + l.dmax);
   a.dscale = dv.io_f32 ? nullptr : reinterpret_cast<float2*>(ws + l.dscale);

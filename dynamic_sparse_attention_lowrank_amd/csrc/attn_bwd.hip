@@ -165,6 +165,54 @@ __global__ __launch_bounds__(256) void rev_count_kernel(BwdArgs a) {
   if (lane == 0) a.counts[row] = cnt;
 }
 
+// One wave per head: order[bh] = the head's key blocks by descending list length
+// (count), ties by ascending block index -- the order in which the dK/dV
+// work-groups take them, so that the longest lists start first and the short ones
+// fill in at the end instead of one long list running on alone (measured at 32K
+// tokens: dK/dV -5 %; dynamic 55K: -4 %).  A counting sort: histogram of the
+// counts (<= NB) in LDS, a descending exclusive scan, then a stable placement in
+// block order, 64 blocks at a time.  Integer work only: deterministic.
+__global__ __launch_bounds__(64) void rev_order_kernel(BwdArgs a) {
+  extern __shared__ int start[];              // [NB + 1]
+  const int NB = a.g.NB, bh = blockIdx.x, lane = threadIdx.x;
+  const int* cnt = a.counts + (size_t)bh * NB;
+  int* ord = a.order + (size_t)bh * NB;
+  for (int c = lane; c <= NB; c += 64) start[c] = 0;
+  __syncthreads();
+  for (int j = lane; j < NB; j += 64) atomicAdd(&start[min(max(cnt[j], 0), NB)], 1);
+  __syncthreads();
+  // start[c] = number of blocks whose count exceeds c (lanes take c descending)
+  int run = 0;
+  for (int top = NB; top >= 0; top -= 64) {
+    const int c = top - lane;
+    const int h = c >= 0 ? start[c] : 0;
+    int incl = h;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (c >= 0) start[c] = run + incl - h;
+    run += __shfl(incl, 63, 64);
+  }
+  __syncthreads();
+  for (int base = 0; base < NB; base += 64) {
+    const int j = base + lane;
+    const int c = j < NB ? min(max(cnt[j], 0), NB) : -1;
+    int before = 0, same = 0;                  // lanes of this chunk with the same count
+#pragma unroll
+    for (int l = 0; l < 64; ++l) {
+      const int cl = __builtin_amdgcn_readlane(c, l);
+      same += cl == c;
+      before += (cl == c) & (l < lane);
+    }
+    if (c >= 0) ord[start[c] + before] = j;
+    __syncthreads();
+    if (c >= 0 && before == same - 1) start[c] += same;
+    __syncthreads();
+  }
+}
+
 // one work-group per head: offsets[bh][j] = sum of counts before j; offsets[bh][NB] = total
 __global__ __launch_bounds__(1024) void rev_scan_kernel(BwdArgs a) {
   __shared__ int part[1024];
@@ -285,9 +333,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ uint32_t red[4];
 
   const Geo g = a.g;
-  const int L = blockIdx.x;                 // natural order (see common.hpp)
+  const int L = blockIdx.x;                 // natural head order (see common.hpp)
   const int bh = L / g.NB;
-  const int j = L - bh * g.NB;
+  const int r = L - bh * g.NB;
+  int j = a.order != nullptr ? a.order[(size_t)bh * g.NB + r] : r;         // longest lists first
+  if ((unsigned)j >= (unsigned)g.NB) j = r;   // (a workspace the prepare phase did not write)
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
@@ -754,6 +804,8 @@ hipError_t launch_prepare_t(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(rev_setbits_kernel, dim3((unsigned)(sgrid < (1u << 20) ? sgrid : (1u << 20))), dim3(256), 0, s, a);
   const unsigned rows4 = (unsigned)(((size_t)a.BH * a.g.NB + 3) / 4);
   hipLaunchKernelGGL(rev_count_kernel, dim3(rows4), dim3(256), 0, s, a);
+  if (a.order != nullptr)
+    hipLaunchKernelGGL(rev_order_kernel, dim3(a.BH), dim3(64), (size_t)(a.g.NB + 1) * sizeof(int), s, a);
   hipLaunchKernelGGL(rev_scan_kernel, dim3(a.BH), dim3(1024), 0, s, a);
   hipLaunchKernelGGL(rev_fill_kernel, dim3(rows4), dim3(256), 0, s, a);
   return hipGetLastError();

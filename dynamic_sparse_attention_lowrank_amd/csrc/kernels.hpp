@@ -170,10 +170,15 @@ struct BwdArgs {
   int32_t* counts;      // [BH, NB]
   int32_t* offsets;     // [BH, NB + 1]
   int32_t* entries;     // [BH, NB * kmax]
+  int32_t* order;       // [BH, NB] key blocks by descending list length (the dK/dV
+                        // work-groups' order), or null: ascending block order
   int words;            // ceil(NB / 32)
   Geo g;
   int BH;
 };
+// longest head (in key blocks) whose dK/dV work-groups take the blocks in
+// descending order of list length; longer heads keep ascending order
+constexpr int kOrderMaxNB = 16383;
 // backward phases: prepare (D + reverse index into the workspace), then dK/dV and
 // dQ, which only read the workspace and may run in either order or concurrently
 hipError_t launch_bwd_prepare(const BwdArgs& a, int io_f32, int d, hipStream_t s);

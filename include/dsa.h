@@ -279,7 +279,9 @@ DSA_API dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, c
  * reverse index keeps 32-bit offsets per head).  It holds D = rowsum(dO * O),
  * the reverse (key block -> query tiles) index of idx (for every key block, the
  * query tiles whose kept set contains it: the sums over queries of dK and dV in
- * the DSV page's stage two, section 4, run over these lists) and, for bf16
+ * the DSV page's stage two, section 4, run over these lists; with the order in
+ * which the dK/dV phase takes the key blocks, longest list first: B*H*NB int32)
+ * and, for bf16
  * inputs, what the fp16 products of the backward need: fp16 copies of dO, of Q
  * (dK/dV phase) and of K (dQ phase), B*H*N*d*2 bytes each; the power-of-two
  * scales of dO, V, Q, K and of V again for the dQ phase (for each, B*H*64 partial
