@@ -179,7 +179,14 @@ __global__ __launch_bounds__(64) void rev_order_kernel(BwdArgs a) {
   int* ord = a.order + (size_t)bh * NB;
   for (int c = lane; c <= NB; c += 64) start[c] = 0;
   __syncthreads();
-  for (int j = lane; j < NB; j += 64) atomicAdd(&start[min(max(cnt[j], 0), NB)], 1);
+  for (int j0 = 0; j0 < NB; j0 += 8 * 64) {   // eight count loads in flight per lane
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + 64 * u + lane < NB ? cnt[j0 + 64 * u + lane] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (v[u] >= 0) atomicAdd(&start[min(v[u], NB)], 1);
+  }
   __syncthreads();
   // start[c] = number of blocks whose count exceeds c (lanes take c descending)
   int run = 0;
@@ -196,9 +203,11 @@ __global__ __launch_bounds__(64) void rev_order_kernel(BwdArgs a) {
     run += __shfl(incl, 63, 64);
   }
   __syncthreads();
+  int c_next = lane < NB ? min(max(cnt[lane], 0), NB) : -1;
   for (int base = 0; base < NB; base += 64) {
     const int j = base + lane;
-    const int c = j < NB ? min(max(cnt[j], 0), NB) : -1;
+    const int c = c_next;
+    c_next = j + 64 < NB ? min(max(cnt[j + 64], 0), NB) : -1;   // the next chunk's, in flight meanwhile
     int before = 0, same = 0;                  // lanes of this chunk with the same count
 #pragma unroll
     for (int l = 0; l < 64; ++l) {
