@@ -536,6 +536,9 @@ def _kernel_label(raw: str) -> str:
         s = re.match(r"ILi(\d+)EE", tail) or re.match(r"<(\d+)>", tail)
         if s and not args:
             args.append(s.group(1))
+        if name == "attn_fwd_pair_kernel":           # bf16 only, template <d, full>
+            dd = re.match(r"ILi(\d+)E", tail) or re.match(r"<(\d+),", tail)
+            args = ["bf16"] + ([dd.group(1)] if dd else [])
         if "Lb1E" in tail[:30] or "true>" in tail[:30]:
             args.append("full")
     return f"{name}<{','.join(args)}>" if args else name

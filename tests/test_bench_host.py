@@ -95,3 +95,17 @@ def test_summaries_refuse_mixed_sources(tmp_path):
     _run_dir(root, "write", "c --copy-probe-mib 8", "b" * 16, rows=[(1, FWD, 1.0)], counter="WRITE_SIZE")
     with pytest.raises(SystemExit):
         bench.summarize(str(root), prof_dir=str(tmp_path / "prof"))
+
+
+def test_kernel_labels():
+    """Short kernel names in the profile summaries, from demangled and mangled symbols."""
+    import bench
+    cases = {
+        "void dsa::(anonymous namespace)::attn_fwd_pair_kernel<128, true>(dsa::FwdArgs)": "attn_fwd_pair_kernel<bf16,128,full>",
+        "_ZN3dsa12_GLOBAL__N_120attn_fwd_pair_kernelILi128ELb1EEEvNS_7FwdArgsE": "attn_fwd_pair_kernel<bf16,128,full>",
+        "void dsa::(anonymous namespace)::attn_fwd_pair_kernel<64, false>(dsa::FwdArgs)": "attn_fwd_pair_kernel<bf16,64>",
+        "void dsa::(anonymous namespace)::attn_fwd_kernel<__bf16, 128, true>(dsa::FwdArgs)": "attn_fwd_kernel<bf16,128,full>",
+        "_ZN3dsa12_GLOBAL__N_115bwd_dkdv_kernelIDF16bLi128ELb1EEEvNS_8BwdArgsE": "bwd_dkdv_kernel<bf16,128,full>",
+    }
+    for raw, want in cases.items():
+        assert bench._kernel_label(raw) == want, raw
