@@ -30,8 +30,9 @@
 //  2'. attn_fwd_pair (bf16, long sequences): one work-group of 8 waves per pair of
 //     neighbouring query tiles, each tile computed as above by 4 waves, walking the
 //     union of the two kept lists so that a block kept by both is gathered once;
-//     chosen when one head's gathered blocks outgrow the caches (kPairMinHeadBytes),
-//     where the gathers are bound by L2-miss bandwidth.
+//     by default chosen when one head's gathered blocks outgrow the caches
+//     (kPairMinHeadBytes), where the gathers are bound by memory bandwidth; the
+//     caller can force either kernel (dsa_set_fwd_kernel).
 // With bf16 inputs the P.V product runs on fp16 matrix cores: v_prep converts
 // V * 2^t, with one power of two per (b, h) that puts the head's largest |v| in
 // [2^14, 2^15) (launch_pow2_scale), so the conversion is exact whatever the size

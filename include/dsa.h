@@ -26,17 +26,18 @@
  *   fp32), B*H <= 65535, and B*H*NB*512 <= 2^32-1 (the work-items of the largest
  *   launch grid) (DSA_ERR_SHAPE).
  * Ownership.  The caller owns every buffer and the stream.  The library never
- *   allocates memory, never synchronises the device and keeps no state between
- *   calls; each call only enqueues kernels on `stream` and returns.  The one
- *   exception is dsa_attn_fwd_noalloc: its workspace is a fixed array in device
- *   memory that the library's code object holds on each GPU it runs on.
+ *   allocates memory and never synchronises the device; each call only enqueues
+ *   kernels on `stream` and returns.  It keeps two pieces of state: the
+ *   process-wide choice of forward kernel (dsa_set_fwd_kernel, default: by size),
+ *   and the workspace of dsa_attn_fwd_noalloc, a fixed array in device memory that
+ *   the library's code object holds on each GPU it runs on.
  * Errors.  All argument checks happen on the host before any HIP call; a failed
  *   check returns its status and enqueues nothing.  A failed kernel launch
  *   returns DSA_ERR_HIP.  Device-side values (k[], idx[]) cannot be checked by
  *   the host without a synchronisation, so the kernels treat them defensively
  *   (documented per entry point) and never access memory out of bounds.
- * Determinism.  For identical inputs every entry point produces bit-identical
- *   outputs (no floating-point atomics).
+ * Determinism.  For identical inputs (and the same forward-kernel choice) every
+ *   entry point produces bit-identical outputs (no floating-point atomics).
  * Concurrency.  Calls on different streams may overlap only if their output
  *   buffers (and workspaces) are disjoint.
  */
@@ -66,7 +67,7 @@ typedef enum {
   DSA_ERR_DTYPE = 5,           /* unknown element type                             */
   DSA_ERR_WORKSPACE = 6,       /* workspace too small or misaligned                */
   DSA_ERR_HIP = 7,             /* a HIP launch failed                              */
-  DSA_ERR_NOT_IMPLEMENTED = 8, /* combination not supported by this build          */
+  DSA_ERR_NOT_IMPLEMENTED = 8, /* combination the library does not support         */
   DSA_ERR_RANK = 9,            /* predictor rank r out of range                    */
   DSA_ERR_SCRATCH = 10,        /* one head needs more than dsa_attn_fwd_noalloc's
                                   fixed device scratch                             */
@@ -276,17 +277,17 @@ DSA_API dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, c
 /*
  * dsa_attn_bwd_workspace_bytes -- device workspace that dsa_attn_bwd needs for
  * this shape and kmax (0 on invalid arguments, including NB*kmax > 2^31-1: the
- * reverse index keeps 32-bit offsets per head).  It holds D = rowsum(dO * O),
+ * reverse index keeps 32-bit offsets per head).  It holds D = rowsum(dO * O);
  * the reverse (key block -> query tiles) index of idx (for every key block, the
  * query tiles whose kept set contains it: the sums over queries of dK and dV in
- * the DSV page's stage two, section 4, run over these lists; with the order in
- * which the dK/dV phase takes the key blocks, longest list first: B*H*NB int32)
- * and, for bf16
- * inputs, what the fp16 products of the backward need: fp16 copies of dO, of Q
- * (dK/dV phase) and of K (dQ phase), B*H*N*d*2 bytes each; the power-of-two
- * scales of dO, V, Q, K and of V again for the dQ phase (for each, B*H*64 partial
- * maxima and B*H float pairs); max |D| per (b, h) with its B*H*64 partial maxima;
- * and D times the fp16 dS scale (B*H*N floats).  Sections are 256-byte aligned.
+ * the DSV page's stage two, section 4, run over these lists) with the order in
+ * which the dK/dV phase takes each head's key blocks, longest list first (B*H*NB
+ * int32); and, for bf16 inputs, what the fp16 products of the backward need:
+ * fp16 copies of dO, of Q (dK/dV phase) and of K (dQ phase), B*H*N*d*2 bytes
+ * each; the power-of-two scales of dO, V, Q, K and of V again for the dQ phase
+ * (for each, B*H*64 partial maxima and B*H float pairs); max |D| per (b, h) with
+ * its B*H*64 partial maxima; and D times the fp16 dS scale (B*H*N floats).
+ * Sections are 256-byte aligned.
  */
 DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
 
@@ -333,11 +334,13 @@ DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const voi
  * be the one prepared with the same idx, k, kmax, O and dO.
  *
  * dsa_attn_bwd_prepare -- D = rowsum(dO * O) and the reverse index (for every
- *   key block, the ascending list of query tiles that kept it) into the
- *   workspace (bf16: also dO's scale and fp16 copy, and max |D|).
+ *   key block, the ascending list of query tiles that kept it, and each head's
+ *   key blocks ordered by descending list length) into the workspace (bf16: also
+ *   dO's scale and fp16 copy, and max |D|).
  * dsa_attn_bwd_dkdv    -- dK, dV: one pass per key block over the query tiles
- *   that kept it (bf16: it first writes V's and Q's scales, Q's fp16 copy and the
- *   scaled D into its sections).
+ *   that kept it, the key blocks of a head taken longest list first so that
+ *   short lists fill in at the end (bf16: it first writes V's and Q's scales, Q's
+ *   fp16 copy and the scaled D into its sections).
  * dsa_attn_bwd_dq      -- dQ: one pass per query tile over its kept blocks
  *   (bf16: it first writes V's and K's scales and K's fp16 copy into its sections).
  */
