@@ -377,7 +377,7 @@ void attn_fwd_kernel(FwdArgs a) {
   ids.init(irow, kk, g.NB, lane);
   int b0 = ids.next(lane);
   int b1 = b0 >= 0 ? ids.next(lane) : -1;
-  f32x16 scur;
+  f32x16 sa, sb;                              // S^T of block j: sa for even j, sb for odd j
   if (b0 >= 0) {
     req_k(b0, 0);
     req_v(b0, 0);
@@ -387,11 +387,14 @@ void attn_fwd_kernel(FwdArgs a) {
     if (kvalid > 0) {
       Frag kf[C::kSteps];
       read_k(0, kf);
-      scores_from(kf, scur);
+      scores_from(kf, sa);
     }
   }
-  int p = 0;                                  // j % 2
-  while (b0 >= 0) {
+  // one iteration; the loop runs it for even and odd j in turn, so the buffer
+  // slots are constants (immediate LDS offsets) and the scores of the next block
+  // land in the other register set (no copy)
+  auto step = [&](auto parity, f32x16& scur, f32x16& snext) __attribute__((always_inline)) {
+    constexpr int p = decltype(parity)::value;          // j % 2
     const int b2 = b1 >= 0 ? ids.next(lane) : -1;
     dma_wait();
     __syncthreads();                          // K(j+1), V(j) landed; iteration j-1 done everywhere
@@ -406,7 +409,6 @@ void attn_fwd_kernel(FwdArgs a) {
       read_k(1 - p, kf);
       read_v(p, vf);
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 snext;
       scores_from(kf, snext);
       PFrag pf[2];
       float bs = block_probs<T, D, FULL>(st, scur, pf, c2, kvalid, h);
@@ -429,11 +431,14 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) st.o[t] = mma_step(vf[t][ks], pf[ks], st.o[t]);
       }
-      scur = snext;
     }
     b0 = b1;
     b1 = b2;
-    p ^= 1;
+    return b0 >= 0;
+  };
+  if (b0 >= 0) {
+    while (step(std::integral_constant<int, 0>{}, sa, sb) && step(std::integral_constant<int, 1>{}, sb, sa)) {
+    }
   }
   __syncthreads();                            // the buffers are free: reuse them for the merge
 
