@@ -416,8 +416,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(Qh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rg = head_rsrc(Gh, (size_t)g.N * D * sizeof(G));
   const __amdgpu_buffer_rsrc_t rs = head_rsrc(w == 0 ? LSEh : Dh, (size_t)g.N * sizeof(float));
-  auto request = [&](int tau, u32x4* lq, u32x4* lg, float (*lst)[64]) {
-    const int base = tile_base(g, tau);
+  auto request = [&](int base, u32x4* lq, u32x4* lg, float (*lst)[64]) {   // tile whose first token is `base`
     dma_tile<G, D, W>(lq, rq, base * D * (int)sizeof(G), goff, w);
     dma_tile<G, D, W>(lg, rg, base * D * (int)sizeof(G), goff, w);
     if (w < 2) dma_row_stats(lst[w], rs, base * 4, soff);
@@ -530,20 +529,26 @@ void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   // the block's query tiles, 64 list entries per vector load (no scalar-load wait per tile)
-  IdList ids;
-  ids.init(list + e0, n, g.NB, lane);
-  if (n > 0) request(ids.next(lane), q0, g0, st0);
+  // (entries are tile ids written by the prepare phase, all valid: the list walk
+  // hands out exactly n of them)
+  TileList ids;
+  ids.init(list + e0, n, g, lane);
+  auto next_base = [&]() {
+    (void)ids.next(lane);
+    return ids.last_base;
+  };
+  if (n > 0) request(next_base(), q0, g0, st0);
   dma_wait();
   __syncthreads();
   // two tiles per trip so that every LDS buffer is a distinct object (the next
   // tile's direct loads never alias the reads of the current one)
   for (int e = 0; e < n; e += 2) {
-    if (e + 1 < n) request(ids.next(lane), q1, g1, st1);
+    if (e + 1 < n) request(next_base(), q1, g1, st1);
     compute(q0, g0, st0);
     dma_wait();
     __syncthreads();
     if (e + 1 >= n) break;
-    if (e + 2 < n) request(ids.next(lane), q0, g0, st0);
+    if (e + 2 < n) request(next_base(), q0, g0, st0);
     compute(q1, g1, st1);
     dma_wait();
     __syncthreads();
@@ -649,8 +654,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x4{};
 
-  auto request = [&](int blk, u32x4* lk, u32x4* lv) {
-    const int base = tile_base(g, blk);
+  auto request = [&](int base, u32x4* lk, u32x4* lv) {   // block whose first token is `base`
     dma_tile<G, D, W>(lk, rk, base * D * (int)sizeof(G), koff, w);   // same layout: G and T have one size
     dma_tile<T, D, W>(lv, rv, base * D * (int)sizeof(T), koff, w);
   };
@@ -753,24 +757,24 @@ void bwd_dq_kernel(BwdArgs a) {
   };
 
   // the kept blocks in idx order, invalid entries skipped (wave-uniform)
-  IdList ids;
-  ids.init(irow, kk, g.NB, lane);
+  TileList ids;
+  ids.init(irow, kk, g, lane);
   auto next_valid = [&]() -> int { return ids.next(lane); };
   int bcur = next_valid();
-  if (bcur >= 0) request(bcur, k0, v0);
+  if (bcur >= 0) request(ids.last_base, k0, v0);
   dma_wait();
   __syncthreads();
   int bnext = bcur >= 0 ? next_valid() : -1;
   // two blocks per trip so that every LDS buffer is a distinct object
   while (bcur >= 0) {
-    if (bnext >= 0) request(bnext, k1, v1);
+    if (bnext >= 0) request(ids.last_base, k1, v1);
     compute(k0, v0);
     dma_wait();
     __syncthreads();
     bcur = bnext;
     if (bcur < 0) break;
     bnext = next_valid();
-    if (bnext >= 0) request(bnext, k0, v0);
+    if (bnext >= 0) request(ids.last_base, k0, v0);
     compute(k1, v1);
     dma_wait();
     __syncthreads();

@@ -339,9 +339,8 @@ void attn_fwd_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(reinterpret_cast<const T*>(a.K) + head_off, (size_t)g.N * D * sizeof(T));
   const size_t hblk = (size_t)g.NB * 64 * D;   // elements per head in the V^T copy
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(reinterpret_cast<const PT*>(a.Vt) + (size_t)bh * hblk, hblk * sizeof(PT));
-  auto req_k = [&](int blk, int slot) {
-    dma_tile<T, D, kFwdWaves>(reinterpret_cast<u32x4*>(smem + slot * kKB), rk, tile_base(g, blk) * D * (int)sizeof(T),
-                              koff, w);
+  auto req_k = [&](int base, int slot) {      // K tile whose first token is `base`
+    dma_tile<T, D, kFwdWaves>(reinterpret_cast<u32x4*>(smem + slot * kKB), rk, base * D * (int)sizeof(T), koff, w);
   };
   auto req_v = [&](int blk, int slot) {
     dma_linear<C::kVInstr, kFwdWaves>(reinterpret_cast<u32x4*>(smem + 2 * kKB + slot * kVB), rv, blk * kVB, w, lane);
@@ -373,15 +372,16 @@ void attn_fwd_kernel(FwdArgs a) {
   };
 
   // the kept blocks in idx order (invalid entries skipped); b0 = block j, b1 = j + 1
-  IdList ids;
-  ids.init(irow, kk, g.NB, lane);
+  TileList ids;
+  ids.init(irow, kk, g, lane);
   int b0 = ids.next(lane);
+  const int base0 = ids.last_base;
   int b1 = b0 >= 0 ? ids.next(lane) : -1;
   f32x16 sa, sb;                              // S^T of block j: sa for even j, sb for odd j
   if (b0 >= 0) {
-    req_k(b0, 0);
+    req_k(base0, 0);
     req_v(b0, 0);
-    if (b1 >= 0) req_k(b1, 1);
+    if (b1 >= 0) req_k(ids.last_base, 1);
     dma_wait();
     __syncthreads();
     if (kvalid > 0) {
@@ -398,7 +398,7 @@ void attn_fwd_kernel(FwdArgs a) {
     const int b2 = b1 >= 0 ? ids.next(lane) : -1;
     dma_wait();
     __syncthreads();                          // K(j+1), V(j) landed; iteration j-1 done everywhere
-    if (b2 >= 0) req_k(b2, p);
+    if (b2 >= 0) req_k(ids.last_base, p);
     if (b1 >= 0) req_v(b1, 1 - p);
     if (kvalid > 0) {
       // every LDS operand of the iteration is requested first: its latency is paid

@@ -249,6 +249,38 @@ struct IdList {
   }
 };
 
+// An IdList of tile ids that also hands out each entry's tile base (its first
+// token, tile_base), computed per lane when the entries are read (on the vector
+// unit, once per 64 entries), so that requesting a tile needs no scalar address
+// arithmetic per block.
+struct TileList {
+  IdList ids;
+  const Geo* g;
+  int tb;                                     // tile base of this lane's entry
+  int last_base;                              // tile base of the id next() returned last
+  __device__ __forceinline__ void bases() {
+    tb = (unsigned)ids.val < (unsigned)ids.nb ? tile_base(*g, ids.val) : 0;
+  }
+  __device__ __forceinline__ void init(const int* list, int count, const Geo& geo, int lane) {
+    g = &geo;
+    ids.init(list, count, geo.NB, lane);
+    bases();
+  }
+  // next valid id (and last_base), or -1 at the end (wave-uniform)
+  __device__ __forceinline__ int next(int lane) {
+    while (ids.mask == 0) {
+      ids.base += 64;
+      if (ids.base >= ids.n) return -1;
+      ids.fill(lane);
+      bases();
+    }
+    const int b = __builtin_ctzll(ids.mask);
+    ids.mask &= ids.mask - 1;
+    last_base = __builtin_amdgcn_readlane(tb, b);
+    return __builtin_amdgcn_readlane(ids.val, b);
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
