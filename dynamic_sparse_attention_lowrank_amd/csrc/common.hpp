@@ -263,6 +263,7 @@ struct TileList {
   }
   __device__ __forceinline__ void init(const int* list, int count, const Geo& geo, int lane) {
     g = &geo;
+    last_base = 0;
     ids.init(list, count, geo.NB, lane);
     bases();
   }
