@@ -69,7 +69,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
   size_t dvec, bitmap, counts, offsets, entries, order, do16, dmax, dscale, vmax, vscale;
-  size_t dabs, dabs_part, du, q16, qmax, qscale, k16, kmaxp, kscale, vmax_q, vscale_q, total;
+  size_t dabs, dabs_part, du, lse2, q16, qmax, qscale, k16, kmaxp, kscale, vmax_q, vscale_q, total;
   int words;
 };
 
@@ -89,13 +89,14 @@ BwdLayout bwd_layout(const Derived& dv, int kmax) {
   l.dscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
   l.vmax = off;    off += dv.io_f32 ? 0 : align256(BH * kDoChunks * sizeof(uint32_t));
   l.vscale = off;  off += dv.io_f32 ? 0 : align256(BH * 2 * sizeof(float));
-  // bf16: the single-pass fp16 dS products (max |D|, scaled D, fp16 copies of Q
+  // bf16: the single-pass fp16 dS products (max |D|, scaled D, LSE in log2 units, fp16 copies of Q
   // for dK/dV and of K for dQ, and their scales; V's scale again for dQ)
   const size_t part = align256(BH * kDoChunks * sizeof(uint32_t)), sc = align256(BH * 2 * sizeof(float));
   const size_t copy = align256(BH * N * (size_t)dv.d * 2);
   l.dabs = off;      off += dv.io_f32 ? 0 : align256(BH * sizeof(uint32_t));
   l.dabs_part = off; off += dv.io_f32 ? 0 : part;
   l.du = off;        off += dv.io_f32 ? 0 : align256(BH * N * sizeof(float));
+  l.lse2 = off;      off += dv.io_f32 ? 0 : align256(BH * N * sizeof(float));
   l.q16 = off;       off += dv.io_f32 ? 0 : copy;
   l.qmax = off;      off += dv.io_f32 ? 0 : part;
   l.qscale = off;    off += dv.io_f32 ? 0 : sc;
@@ -416,6 +417,7 @@ dsa_status bwd_common(int phases, const dsa_shape* shape, const void* Q, const v
   a.dabs = reinterpret_cast<uint32_t*>(at(l.dabs));
   a.dabs_part = reinterpret_cast<uint32_t*>(at(l.dabs_part));
   a.Du = reinterpret_cast<float*>(at(l.du));
+  a.Lse2 = reinterpret_cast<float*>(at(l.lse2));
   a.q16 = at(l.q16);
   a.qmax = reinterpret_cast<uint32_t*>(at(l.qmax));
   a.qscale = reinterpret_cast<float2*>(at(l.qscale));

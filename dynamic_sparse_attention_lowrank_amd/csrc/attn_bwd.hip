@@ -282,14 +282,22 @@ __global__ __launch_bounds__(256) void rev_fill_kernel(BwdArgs a) {
   }
 }
 
-// Du = D * 2^u per (b, h) for the dK/dV phase (bf16 inputs); grid (blocks, heads)
+// The dK/dV phase's per-token statistics (bf16 inputs): Du = D * 2^u per (b, h),
+// and LSE * log2(e), the fp32 product the exponent of P takes per (query, key)
+// pair otherwise (written once per token instead); grid (blocks, heads)
 template <int D>
 __global__ __launch_bounds__(256) void scale_d_kernel(BwdArgs a) {
   const int bh = blockIdx.y;
   const float up = pow2f(ds_exponent(a.dscale[bh], a.vscale[bh], a.dabs[bh], kLog2D<D>));
-  const float* __restrict__ src = a.Dvec + (size_t)bh * a.g.N;
-  float* __restrict__ dst = a.Du + (size_t)bh * a.g.N;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < a.g.N; i += gridDim.x * 256) dst[i] = src[i] * up;
+  const size_t h = (size_t)bh * a.g.N;
+  const float* __restrict__ src = a.Dvec + h;
+  const float* __restrict__ lse = a.LSE + h;
+  float* __restrict__ dst = a.Du + h;
+  float* __restrict__ l2 = a.Lse2 + h;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < a.g.N; i += gridDim.x * 256) {
+    dst[i] = src[i] * up;
+    l2[i] = lse[i] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------- 4. dK, dV
@@ -338,7 +346,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DT = D / 16;                  // 16-wide output tiles over d
   __shared__ u32x4 q0[CG::kRowChunks], q1[CG::kRowChunks];
   __shared__ u32x4 g0[CG::kRowChunks], g1[CG::kRowChunks];
-  __shared__ float st0[2][64], st1[2][64];    // [LSE, D (* 2^u)][query row]
+  __shared__ float st0[2][64], st1[2][64];    // [LSE (* log2 e), D (* 2^u)][query row]
   __shared__ uint32_t red[4];
 
   const Geo g = a.g;
@@ -353,7 +361,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const size_t head_off = (size_t)bh * g.N * D;
   const G* __restrict__ Qh = (kHalf ? reinterpret_cast<const G*>(a.q16) : reinterpret_cast<const G*>(a.Q)) + head_off;
   const G* __restrict__ Gh = (kHalf ? reinterpret_cast<const G*>(a.dO16) : reinterpret_cast<const G*>(a.dO)) + head_off;
-  const float* __restrict__ LSEh = a.LSE + (size_t)bh * g.N;
+  // row statistics: LSE (fp32 inputs) or LSE * log2(e) (bf16), and D or D * 2^u
+  const float* __restrict__ LSEh = (kHalf ? a.Lse2 : a.LSE) + (size_t)bh * g.N;
   const float* __restrict__ Dh = (kHalf ? a.Du : a.Dvec) + (size_t)bh * g.N;
   const int jbase = tile_base(g, j);
 
@@ -482,7 +491,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lst[1][r0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p = fast_exp2(fmaf(sacc[mt][i], c2, -l4[i] * kLog2e));
+          float p = fast_exp2(fmaf(sacc[mt][i], c2, kHalf ? -l4[i] : -l4[i] * kLog2e));
           if constexpr (!FULL) p = (r0 + i < g.T) ? p : 0.f;      // padding query rows
           pv[4 * hf + i] = p;
           sv[4 * hf + i] = p * fmaf(pacc[mt][i], dpinv, -d4[i]);

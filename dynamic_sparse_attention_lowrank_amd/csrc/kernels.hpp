@@ -158,6 +158,7 @@ struct BwdArgs {
   uint32_t* dabs;       // [BH] bits of max |D| (written by prepare)
   uint32_t* dabs_part;  // [BH, kDoChunks] its partial maxima
   float* Du;            // [BH, N] D * 2^u_bh, the scaled D of the dK/dV phase
+  float* Lse2;          // [BH, N] LSE * log2(e) (fp32 product), the dK/dV phase's row statistic
   void* q16;            // [BH, N, d] fp16 Q * 2^a_bh (dK/dV phase)
   uint32_t* qmax;       // [BH, kDoChunks]
   float2* qscale;       // [BH] (2^a_bh, 2^-a_bh)

@@ -286,7 +286,8 @@ DSA_API dsa_status dsa_attn_fwd_noalloc(const dsa_shape* shape, const void* Q, c
  * fp16 copies of dO, of Q (dK/dV phase) and of K (dQ phase), B*H*N*d*2 bytes
  * each; the power-of-two scales of dO, V, Q, K and of V again for the dQ phase
  * (for each, B*H*64 partial maxima and B*H float pairs); max |D| per (b, h) with
- * its B*H*64 partial maxima; and D times the fp16 dS scale (B*H*N floats).
+ * its B*H*64 partial maxima; D times the fp16 dS scale and LSE times log2(e)
+ * (B*H*N floats each).
  * Sections are 256-byte aligned.
  */
 DSA_API size_t dsa_attn_bwd_workspace_bytes(const dsa_shape* shape, int32_t kmax);
@@ -340,7 +341,7 @@ DSA_API dsa_status dsa_attn_bwd(const dsa_shape* shape, const void* Q, const voi
  * dsa_attn_bwd_dkdv    -- dK, dV: one pass per key block over the query tiles
  *   that kept it, the key blocks of a head taken longest list first so that
  *   short lists fill in at the end (bf16: it first writes V's and Q's scales, Q's
- *   fp16 copy and the scaled D into its sections).
+ *   fp16 copy, the scaled D and LSE * log2(e) into its sections).
  * dsa_attn_bwd_dq      -- dQ: one pass per query tile over its kept blocks
  *   (bf16: it first writes V's and K's scales and K's fp16 copy into its sections).
  */

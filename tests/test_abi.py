@@ -196,7 +196,7 @@ def test_workspace_formula(L):
     """D (fp32 per token) + bitmap (NB x ceil(NB/32) words) + counts + offsets + entries
     + the dK/dV block order (+ for bf16 inputs: fp16 copies of dO, Q and K; for dO, V, Q, K and V again 64
     partial maxima and one scale pair per (b, h); max |D| per (b, h) with its 64
-    partial maxima; D * 2^u per token), each section rounded up to 256 bytes."""
+    partial maxima; D * 2^u and LSE * log2(e) per token), each section rounded up to 256 bytes."""
     sh = _shape(L, B=2, H=3, d=128, Lt=3, Lh=16, Lw=24, tt=1, th=8, tw=8, io=1)
     BH, N, NB, kmax = 6, 3 * 16 * 24, 18, 5
     r = lambda x: (x + 255) // 256 * 256
@@ -204,7 +204,7 @@ def test_workspace_formula(L):
             + r(BH * NB * 4))                                # the dK/dV block order
     part, pair, copy = r(BH * 64 * 4), r(BH * 2 * 4), r(BH * N * 128 * 2)
     bf16_extra = (copy + 2 * (part + pair)                  # fp16 dO; scales of dO and V
-                  + r(BH * 4) + part + r(BH * N * 4)        # max |D|, its partial maxima, D * 2^u
+                  + r(BH * 4) + part + 2 * r(BH * N * 4)    # max |D|, its partial maxima, D * 2^u, LSE log2 e
                   + 2 * (copy + part + pair)                # Q and K: fp16 copy and scale
                   + part + pair)                            # V's scale for the dQ phase
     assert L.lib.dsa_attn_bwd_workspace_bytes(ctypes.byref(sh), kmax) == want + bf16_extra
