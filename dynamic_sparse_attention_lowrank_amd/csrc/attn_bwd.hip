@@ -30,8 +30,9 @@
 //                transposed from LDS);
 //   4. dQ:       one work-group (4 waves, 16 queries each) per query tile walks
 //                its kept blocks (S^T = K Q^T, dP^T = V dO^T; dQ^T += K^T dS^T).
-// Both stream their tiles through double-buffered LDS filled by direct
-// global->LDS loads, one tile ahead of the computation.
+// Both stream their tiles through LDS filled by direct global->LDS loads, one
+// tile ahead of the computation (double-buffered; dQ's V tile, read only in its
+// first products, single-buffered).
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -309,6 +310,7 @@ __global__ __launch_bounds__(256) void scale_d_kernel(BwdArgs a) {
 // two waves per SIMD for 16-bit inputs; the fp32 variants (parity checks only)
 // need more than 256 registers and run at one
 template <typename T> constexpr int kWavesPerSimd = sizeof(T) == 2 ? 2 : 1;
+template <typename T> constexpr int kDqWavesPerSimd = sizeof(T) == 2 ? 3 : 1;
 
 template <typename T> struct GradType;
 template <> struct GradType<bf16> { typedef f16 type; };
@@ -579,11 +581,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 5. dQ
-// One work-group of 4 waves per query tile, two waves per SIMD; wave w owns
-// queries 16w..16w+15, whose Q and dO rows stay in registers as the B operands of
-// the 16x16x32 products S^T = K Q^T and dP^T = V dO^T.  The kept blocks stream
-// through two LDS buffers (K and V rows), filled by direct global->LDS loads one
-// block ahead.  With bf16 inputs K comes from this phase's fp16 copy (K * 2^b),
+// One work-group of 4 waves per query tile, three work-groups per CU (16-bit
+// inputs); wave w owns queries 16w..16w+15, whose Q and dO rows stay in registers
+// as the B operands of the 16x16x32 products S^T = K Q^T and dP^T = V dO^T.  The
+// kept blocks stream through LDS, filled by direct global->LDS loads: K rows (read
+// in both halves of a block) in two buffers, one block ahead; V rows (read only by
+// dP^T) in one, the next block's requested once every wave is past its dP^T
+// products.  One V buffer keeps the work-group at 48 KB of LDS, so three fit on a
+// CU (measured at 32K tokens: -4 % against two buffers at two per CU, outputs
+// bit-identical).  With bf16 inputs K comes from this phase's fp16 copy (K * 2^b),
 // Q is converted to fp16 with a power of two per query tile, dP^T = V dO^T stays
 // bf16, and dS^T * 2^u is rounded to fp16.  Per block and wave:
 //   S^T, dP^T (64 keys x 16 queries)   A = K / V rows (ds_read_b128), 4 x 4 MFMA each
@@ -591,7 +597,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 //   dQ^T += K^T dS^T                   B = dS^T straight from the S^T registers,
 //                                      A = K read transposed (ds_read_b64_tr_b16)
 template <typename T, int D, bool FULL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<T>, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<T>, 3)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int W = 4;
   typedef typename GradType<T>::type G;      // K tiles, Q and dS operands
@@ -603,7 +609,7 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int DT = D / 16;
   constexpr bool kFast = sizeof(T) == 2;
   __shared__ u32x4 k0[CG::kRowChunks], k1[CG::kRowChunks];
-  __shared__ u32x4 v0[C::kRowChunks], v1[C::kRowChunks];
+  __shared__ u32x4 vt[C::kRowChunks];          // one V buffer: read in the first products only
   __shared__ uint32_t red[4];
 
   const Geo g = a.g;
@@ -663,11 +669,11 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x4{};
 
-  auto request = [&](int base, u32x4* lk, u32x4* lv) {   // block whose first token is `base`
+  auto request_k = [&](int base, u32x4* lk) {   // block whose first token is `base`
     dma_tile<G, D, W>(lk, rk, base * D * (int)sizeof(G), koff, w);   // same layout: G and T have one size
-    dma_tile<T, D, W>(lv, rv, base * D * (int)sizeof(T), koff, w);
   };
-  auto compute = [&](const u32x4* lk, const u32x4* lv) {
+  auto request_v = [&](int base) { dma_tile<T, D, W>(vt, rv, base * D * (int)sizeof(T), koff, w); };
+  auto compute = [&](const u32x4* lk, const u32x4* lv, auto&& mid) {
     // S^T and dP^T: lane holds query column qr, key rows 16mt + 4q + i
     f32x4 sacc[4], pacc[4];
     GFrag ka[4];                               // transposed K operands of the first steps (prefetched)
@@ -698,6 +704,7 @@ void bwd_dq_kernel(BwdArgs a) {
         ka[2 * k] = frag16_tr_fast<G, D>(lk, 0, trl ^ (32 * k), (G*)nullptr);
         ka[2 * k + 1] = frag16_tr_fast<G, D>(lk, 1, trl ^ (32 * k), (G*)nullptr);
       }
+      mid();
     } else {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -710,6 +717,7 @@ void bwd_dq_kernel(BwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      mid();
     }
     // dS^T (* 2^u) as B operands: k-slot e of step ks <-> key 32ks + 16(e/4) + 4q + e%4
     GFrag sf[2];
@@ -770,26 +778,38 @@ void bwd_dq_kernel(BwdArgs a) {
   ids.init(irow, kk, g, lane);
   auto next_valid = [&]() -> int { return ids.next(lane); };
   int bcur = next_valid();
-  if (bcur >= 0) request(ids.last_base, k0, v0);
+  if (bcur >= 0) {
+    request_k(ids.last_base, k0);
+    request_v(ids.last_base);
+  }
   dma_wait();
   __syncthreads();
   int bnext = bcur >= 0 ? next_valid() : -1;
-  // two blocks per trip so that every LDS buffer is a distinct object
+  int nbase = ids.last_base;
+  // V of the next block is requested once every wave has finished its S^T, dP^T
+  // products (the only reads of V); K, read in both halves, is double-buffered
+  auto mid = [&]() {
+    __syncthreads();
+    if (bnext >= 0) request_v(nbase);
+  };
+  // two blocks per trip so that every K buffer is a distinct object
   while (bcur >= 0) {
-    if (bnext >= 0) request(ids.last_base, k1, v1);
-    compute(k0, v0);
+    if (bnext >= 0) request_k(nbase, k1);
+    compute(k0, vt, mid);
     dma_wait();
     __syncthreads();
     bcur = bnext;
     if (bcur < 0) break;
     bnext = next_valid();
-    if (bnext >= 0) request(ids.last_base, k0, v0);
-    compute(k1, v1);
+    nbase = ids.last_base;
+    if (bnext >= 0) request_k(nbase, k0);
+    compute(k1, vt, mid);
     dma_wait();
     __syncthreads();
     bcur = bnext;
     if (bcur < 0) break;
     bnext = next_valid();
+    nbase = ids.last_base;
   }
 
   // store: lane holds query column qr, d rows 16t + 4q + i
